@@ -1,0 +1,274 @@
+"""Oracle: a plain fp64 CPU reference for load-balanced split-KV decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP library and never imports it; inputs come from numpy arrays that the
+caller made with the seeded workload generator.
+
+What it computes is written in ``oracle.c`` next to this file, each function
+citing the passage of the pages it follows ("HPC-Ops x SGLang", sections
+"Attention: load balancing for variable-length decode" and "Scheduling around
+live KV work"; "Hy3 preview full-stack inference optimization", section 2.1.1).
+
+Arrays:
+  q          [B, H_q, D]              uint16 (bf16 bits) or uint8 (e4m3 bytes)
+  k_pages    [num_pages, H_kv, 64, D] same element type as q
+  v_pages    [num_pages, H_kv, 64, D]
+  q_scale    [B, H_q] float32          fp8 only
+  k_scale    [num_pages, H_kv, 64] float32, v_scale likewise (fp8 only)
+  page_table [B, max_pages] int32
+  seq_lens   [B] int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+TILE = 64
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-Wall", "-shared", "-fPIC",
+             _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("kv_fp8", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("sm_scale", ctypes.c_double),
+    ]
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+            dp = ctypes.POINTER(_Dims)
+            lib.orc_bf16_value.argtypes = [i32]
+            lib.orc_bf16_value.restype = f64
+            lib.orc_e4m3_value.argtypes = [i32]
+            lib.orc_e4m3_value.restype = f64
+            lib.orc_attend_range.argtypes = [dp, P, P, P, P, P, P, P, i32, i32, i32, i32, P, P]
+            lib.orc_attend_range.restype = ctypes.c_int
+            lib.orc_attention.argtypes = [dp, P, P, P, P, P, P, P, P, P, i32, P, P]
+            lib.orc_attention.restype = ctypes.c_int
+            lib.orc_lse_merge.argtypes = [i32, i32, P, P, P, P]
+            lib.orc_lse_merge.restype = None
+            lib.orc_plan_words.argtypes = [i32, i32, i32]
+            lib.orc_plan_words.restype = i64
+            lib.orc_plan.argtypes = [P, i32, i32, i32, i32, P, i64]
+            lib.orc_plan.restype = i64
+            lib.orc_partials.argtypes = [dp, P, P, P, P, P, P, P, P, i32, P, P]
+            lib.orc_partials.restype = ctypes.c_int
+            lib.orc_combine.argtypes = [dp, P, i32, P, P, P, P]
+            lib.orc_combine.restype = ctypes.c_int
+            lib.orc_max_threads.argtypes = []
+            lib.orc_max_threads.restype = i32
+            lib.orc_set_threads.argtypes = [i32]
+            lib.orc_set_threads.restype = None
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+class _Inputs:
+    """Validated, contiguous views of one attention problem."""
+
+    def __init__(self, q, k_pages, v_pages, page_table, num_kv_heads, sm_scale,
+                 q_scale=None, k_scale=None, v_scale=None):
+        fp8 = q.dtype == np.uint8
+        et = np.uint8 if fp8 else np.uint16
+        if q.dtype not in (np.uint8, np.uint16):
+            raise TypeError("q must hold bf16 bits (uint16) or e4m3 bytes (uint8)")
+        self.q = _c(q, et)
+        self.k = _c(k_pages, et)
+        self.v = _c(v_pages, et)
+        self.pt = _c(page_table, np.int32)
+        B, Hq, D = self.q.shape
+        if self.k.shape[1:] != (num_kv_heads, TILE, D) or self.v.shape != self.k.shape:
+            raise ValueError("k/v pools must be [num_pages, H_kv, 64, D]")
+        if Hq % num_kv_heads:
+            raise ValueError("H_q must be a multiple of H_kv")
+        if fp8:
+            if q_scale is None or k_scale is None or v_scale is None:
+                raise ValueError("fp8 inputs need q_scale, k_scale and v_scale")
+            self.qs = _c(q_scale, np.float32)
+            self.ks = _c(k_scale, np.float32)
+            self.vs = _c(v_scale, np.float32)
+        else:
+            self.qs = self.ks = self.vs = None
+        self.dims = _Dims(B, Hq, num_kv_heads, D, self.pt.shape[1], self.k.shape[0],
+                          1 if fp8 else 0, 0, float(sm_scale))
+        self.G = Hq // num_kv_heads
+
+    def args(self):
+        return (ctypes.byref(self.dims), _ptr(self.q), _ptr(self.qs), _ptr(self.k),
+                _ptr(self.v), _ptr(self.ks), _ptr(self.vs), _ptr(self.pt))
+
+
+def bf16_value(bits: int) -> float:
+    return _load().orc_bf16_value(int(bits))
+
+
+def e4m3_value(code: int) -> float:
+    return _load().orc_e4m3_value(int(code))
+
+
+def e4m3_table() -> np.ndarray:
+    """fp64 value of each of the 256 OCP E4M3FN codes."""
+    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def attend_range(q, k_pages, v_pages, page_table, b, h, tok0, tok1, *, num_kv_heads,
+                 sm_scale, q_scale=None, k_scale=None, v_scale=None):
+    """Attention of the G query heads of (request b, KV head h) over tokens
+    [tok0, tok1).  Returns (o [G, D], lse [G]) in fp64."""
+    x = _Inputs(q, k_pages, v_pages, page_table, num_kv_heads, sm_scale,
+                q_scale, k_scale, v_scale)
+    o = np.zeros((x.G, x.dims.head_dim), np.float64)
+    lse = np.zeros((x.G,), np.float64)
+    rc = _load().orc_attend_range(*x.args(), int(b), int(h), int(tok0), int(tok1),
+                                  _ptr(o), _ptr(lse))
+    if rc:
+        raise RuntimeError("orc_attend_range failed")
+    return o, lse
+
+
+def attention(q, k_pages, v_pages, page_table, seq_lens, *, num_kv_heads, sm_scale,
+              q_scale=None, k_scale=None, v_scale=None, pairs=None):
+    """Decode attention of every request over its whole live KV.
+
+    pairs: optional iterable of (b, h) to compute; other rows stay NaN.
+    Returns (out [B, H_q, D], lse [B, H_q]) in fp64."""
+    x = _Inputs(q, k_pages, v_pages, page_table, num_kv_heads, sm_scale,
+                q_scale, k_scale, v_scale)
+    lens = _c(seq_lens, np.int32)
+    B, Hq, D = x.q.shape
+    out = np.full((B, Hq, D), np.nan, np.float64)
+    lse = np.full((B, Hq), np.nan, np.float64)
+    pr = None if pairs is None else np.ascontiguousarray(np.asarray(pairs, np.int32).reshape(-1, 2))
+    n = 0 if pr is None else pr.shape[0]
+    rc = _load().orc_attention(*x.args(), _ptr(lens), _ptr(pr), n, _ptr(out), _ptr(lse))
+    if rc:
+        raise RuntimeError("orc_attention failed")
+    return out, lse
+
+
+def lse_merge(lse, o):
+    """Merge n partials (lse [n], o [n, W]) under the global softmax."""
+    lse = _c(lse, np.float64)
+    o = _c(o, np.float64).reshape(lse.shape[0], -1)
+    out = np.zeros((o.shape[1],), np.float64)
+    out_lse = np.zeros((1,), np.float64)
+    _load().orc_lse_merge(lse.shape[0], o.shape[1], _ptr(lse), _ptr(o), _ptr(out), _ptr(out_lse))
+    return out, float(out_lse[0])
+
+
+def plan_words(batch: int, num_kv_heads: int, num_bins: int) -> int:
+    return int(_load().orc_plan_words(batch, num_kv_heads, num_bins))
+
+
+def plan(seq_lens, num_kv_heads: int, num_bins: int, min_tiles: int) -> np.ndarray:
+    """The task map as int32 words (layout in oracle.c)."""
+    lens = _c(seq_lens, np.int32)
+    n = plan_words(lens.shape[0], num_kv_heads, num_bins)
+    m = np.zeros((n,), np.int32)
+    rc = _load().orc_plan(_ptr(lens), lens.shape[0], num_kv_heads, num_bins, min_tiles,
+                          _ptr(m), n)
+    if rc < 0:
+        raise ValueError("orc_plan rejected its input (code %d)" % rc)
+    return m
+
+
+def parse_map(words, num_bins: int) -> dict:
+    """Split task-map words into named arrays (the oracle's own reading)."""
+    w = np.asarray(words, np.int32)
+    B, Hkv = int(w[5]), int(w[6])
+    S = B * Hkv
+    o = 8
+    d = {"T": int(w[0]), "P_eff": int(w[1]), "q": int(w[2]), "r": int(w[3]),
+         "num_desc": int(w[4]), "B": B, "H_kv": Hkv, "err": int(w[7])}
+    d["seq_lens"] = w[o:o + B]; o += B
+    d["bin_desc_off"] = w[o:o + num_bins + 1]; o += num_bins + 1
+    d["seg_desc_off"] = w[o:o + S + 1]; o += S + 1
+    d["desc"] = w[o:o + 4 * (S + num_bins - 1)].reshape(-1, 4)[: d["num_desc"]]
+    return d
+
+
+def partials(q, k_pages, v_pages, page_table, task_map, num_bins, *, num_kv_heads,
+             sm_scale, q_scale=None, k_scale=None, v_scale=None):
+    """Per-descriptor partial (o, lse) following a task map."""
+    x = _Inputs(q, k_pages, v_pages, page_table, num_kv_heads, sm_scale,
+                q_scale, k_scale, v_scale)
+    m = _c(task_map, np.int32)
+    nd = int(m[4])
+    po = np.zeros((max(nd, 1), x.G, x.dims.head_dim), np.float64)
+    pl = np.zeros((max(nd, 1), x.G), np.float64)
+    rc = _load().orc_partials(*x.args(), _ptr(m), int(num_bins), _ptr(po), _ptr(pl))
+    if rc:
+        raise RuntimeError("orc_partials failed")
+    return po[:nd], pl[:nd]
+
+
+def combine(task_map, num_bins, part_o, part_lse, *, num_q_heads, head_dim):
+    """Merge per-descriptor partials into (out [B, H_q, D], lse [B, H_q])."""
+    m = _c(task_map, np.int32)
+    B, Hkv = int(m[5]), int(m[6])
+    dims = _Dims(B, num_q_heads, Hkv, head_dim, 0, 0, 0, 0, 0.0)
+    po = _c(part_o, np.float64)
+    pl = _c(part_lse, np.float64)
+    if po.size == 0:
+        po = np.zeros((1,), np.float64)
+        pl = np.zeros((1,), np.float64)
+    out = np.zeros((B, num_q_heads, head_dim), np.float64)
+    lse = np.zeros((B, num_q_heads), np.float64)
+    rc = _load().orc_combine(ctypes.byref(dims), _ptr(m), int(num_bins), _ptr(po), _ptr(pl),
+                             _ptr(out), _ptr(lse))
+    if rc:
+        raise RuntimeError("orc_combine failed")
+    return out, lse
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().orc_set_threads(int(n))
