@@ -1,0 +1,276 @@
+"""Benchmark: load-balanced split-KV decode attention on one MI355X.
+
+A step is one decode step of the whole path over one batch: hpcattn_plan
+once, then hpcattn_decode + hpcattn_combine for every layer, each layer with
+its own KV pool (so the 256 MB Infinity Cache cannot serve repeats).  Inputs
+are resident in HBM before the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload mixed|single_long|heavy_tail|fp8]
+                    [--num-bins P] [--min-tiles m] [--ablation] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is the step's KV-read throughput (live KV
+bytes of all layers / step time); `roofline` is for the decode kernel, timed
+per launch with HIP events on the stream it runs on; `cpu_baseline` is the
+fp64 oracle on the host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + KV-read GB/s (% HBM peak), mixed-length GQA batch"
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_mixed_traffic.md")
+DECODE_SRC = os.path.join(ROOT, "load_balanced_split_amd", "csrc", "decode.hip")
+
+DESCRIPTIONS = {
+    "mixed": "mixed-length: 64 requests, KV lens log-uniform in [256, 32768] (seed 0), "
+             "8 KV / 64 Q heads, head_dim 128, bf16, page 64, shuffled pages, "
+             "32 layers with distinct KV pools, one task map per step",
+    "single_long": "single long: 1 request of 131072 tokens, 8 KV / 64 Q heads, head_dim 128, "
+                   "bf16, page 64, shuffled pages, 4 rotating KV pools",
+    "heavy_tail": "heavy-tail: 120 requests of 1024+-10% and 8 of 65536 tokens, 8 KV / 64 Q "
+                  "heads, head_dim 128, bf16, page 64, 4 rotating KV pools",
+    "fp8": "fp8 KV: 32 requests, KV lens log-uniform in [1024, 131072], 8 KV / 64 Q heads, "
+           "head_dim 128, e4m3 Q/K/V with per-token per-head fp32 scales, page 64, "
+           "4 rotating KV pools",
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--num-bins", type=int, default=None)
+    ap.add_argument("--min-tiles", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers (distinct KV pools) per step; default 32 for mixed, else 1")
+    ap.add_argument("--pools", type=int, default=4,
+                    help="rotating KV pools for the one-layer workloads")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--ablation", action="store_true",
+                    help="also sweep the static split-KV baseline on the same inputs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def traffic_from_profile():
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current decode source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    text = open(PROFILE_TRAFFIC).read()
+    m = re.search(r"decode_source_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t:
+        return None
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    return float(t.group(1)) if sha == m.group(1) else None
+
+
+def cpu_baseline(prob, budget_s: float):
+    """The fp64 oracle, as it stands, on all host cores over a bounded sample
+    of layer 0: whole (request, KV head) pairs in a seeded order until the
+    time budget is spent.  Returns the KV GB/s it sustained."""
+    import numpy as np
+
+    import oracle
+    from load_balanced_split_amd import workloads as wl
+
+    w = prob.workload
+    h = dict(q=wl.as_numpy(prob.q), k_pages=wl.as_numpy(prob.k_pages[0]),
+             v_pages=wl.as_numpy(prob.v_pages[0]), page_table=prob.page_table,
+             seq_lens=prob.seq_lens)
+    if w.kv_dtype == "fp8":
+        h.update(q_scale=wl.as_numpy(prob.q_scale), k_scale=wl.as_numpy(prob.k_scale[0]),
+                 v_scale=wl.as_numpy(prob.v_scale[0]))
+    rng = np.random.default_rng(7)
+    pairs = [(int(b), hh) for b in rng.permutation(len(prob.seq_lens))
+             for hh in range(w.num_kv_heads)]
+    cores = oracle.max_threads()
+    done_tok, spent, i = 0, 0.0, 0
+    chunk = max(cores, 8)
+    while i < len(pairs) and spent < budget_s:
+        sel = pairs[i:i + chunk]
+        t0 = time.perf_counter()
+        oracle.attention(h["q"], h["k_pages"], h["v_pages"], h["page_table"], h["seq_lens"],
+                         num_kv_heads=w.num_kv_heads, sm_scale=prob.sm_scale,
+                         q_scale=h.get("q_scale"), k_scale=h.get("k_scale"),
+                         v_scale=h.get("v_scale"), pairs=sel)
+        spent += time.perf_counter() - t0
+        done_tok += sum(int(prob.seq_lens[b]) for b, _ in sel)
+        i += len(sel)
+    per_tok_head = wl.kv_bytes_per_token(w) // w.num_kv_heads
+    gbs = done_tok * per_tok_head / spent / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "layer 0, %d of %d (request, KV head) pairs (%d KV tokens), %.1f s of "
+                      "fp64 C/OpenMP work" % (i, len(pairs), done_tok, spent)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from load_balanced_split_amd import hpcattn as H
+    from load_balanced_split_amd import runner, workloads as wl
+
+    torch.cuda.set_device(0)
+    name = args.workload
+    w = wl.WORKLOADS[name]
+    layers = args.layers if args.layers is not None else (w.layers if name == "mixed" else 1)
+    pools = layers if name == "mixed" else max(1, args.pools)
+    prob = wl.make_problem(name, seed=args.seed, device="cuda", layers=pools)
+    run = runner.DecodeRunner(prob, num_bins=args.num_bins, min_tiles=args.min_tiles)
+    stream = torch.cuda.current_stream()
+    live_tokens = int(prob.seq_lens.sum())
+    kv_bytes_layer = live_tokens * wl.kv_bytes_per_token(w)
+
+    def step(k, ev=None):
+        run.plan()
+        for layer in range(layers):
+            pool = (k * layers + layer) % pools
+            if ev is not None:
+                ev[layer][0].record(stream)
+            run.decode(pool)
+            if ev is not None:
+                ev[layer][1].record(stream)
+            run.combine()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    step_ms, dec_ms = [], []
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        step(args.warmup + k, ev)
+        s1.record(stream)
+        s1.synchronize()
+        step_ms.append(s0.elapsed_time(s1))
+        dec_ms.extend(e0.elapsed_time(e1) for e0, e1 in ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    # Plan and combine alone, for the breakdown (outside the timed steps).
+    def time_op(fn, reps=20):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+    plan_ms = time_op(run.plan)
+    combine_ms = time_op(run.combine)
+
+    med_step = statistics.median(step_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    value = kv_bytes_layer * layers / (med_step * 1e-3) / 1e9
+    achieved = kv_bytes_layer / (dec_avg * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med_step, 4),
+        "us_per_step": round(med_step * 1e3, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if w.kv_dtype == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": DESCRIPTIONS[name],
+            "batch": int(prob.seq_lens.shape[0]),
+            "layers": layers,
+            "live_kv_tokens": live_tokens,
+            "kv_bytes_per_layer": kv_bytes_layer,
+            "num_bins": run.num_bins,
+            "min_tiles": run.min_tiles,
+            "num_desc": run.num_desc(),
+            "seed": args.seed,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "breakdown_us": {"plan": round(plan_ms * 1e3, 2),
+                         "decode_avg": round(dec_avg * 1e3, 2),
+                         "combine": round(combine_ms * 1e3, 2),
+                         "step_min": round(min(step_ms) * 1e3, 1),
+                         "step_p90": round(sorted(step_ms)[int(0.9 * (len(step_ms) - 1))] * 1e3, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(),
+                     "kernel": "decode_kernel (one launch = one layer's live KV)"},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if args.ablation:
+        out["ablation"] = static_sweep(run, prob, layers, pools, stream, dec_avg)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=10):
+    """Time the static split-KV baseline (decode + combine) at every sweep
+    point against dynamic decode + combine on the same pools."""
+    import torch
+
+    def timed(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        fn(0)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for r in range(reps):
+            fn((r + 1) % pools)
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    def dyn(pool):
+        run.decode(pool)
+        run.combine()
+
+    res = {"dynamic_us": round(timed(dyn), 2), "static_us": {}}
+    for S in (1, 2, 4, 8, 16, 32, 64, 128):
+        res["static_us"]["splits=%d" % S] = round(timed(lambda p: run.static(0, S, p)), 2)
+    for C in (256, 512, 1024, 2048, 4096, 8192):
+        res["static_us"]["chunk=%d" % C] = round(timed(lambda p: run.static(1, C, p)), 2)
+    best = min(res["static_us"], key=res["static_us"].get)
+    res["best_static"] = best
+    res["speedup_vs_best_static"] = round(res["static_us"][best] / res["dynamic_us"], 3)
+    return res
+
+
+if __name__ == "__main__":
+    main()

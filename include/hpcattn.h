@@ -1,0 +1,225 @@
+/*
+ * hpcattn.h -- C ABI of load-balanced split-KV decode attention over a paged
+ * GQA KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method ("HPC-Ops x SGLang: Tencent Hunyuan open-sources high-performance
+ * Attention, Router GEMM and MoE operators", sections "Attention: load
+ * balancing for variable-length decode" and "Scheduling around live KV work";
+ * "Hy3 preview full-stack inference optimization", section 2.1.1 "Attention
+ * dynamic scheduling"):
+ *
+ *   1. hpcattn_plan     once per decode step: cut each request's live KV into
+ *                       64-token tiles, count them over all requests and KV
+ *                       heads, split the total into near-equal bins, one per
+ *                       persistent workgroup, and write the task map.
+ *   2. hpcattn_decode   per layer: each persistent workgroup drains its bin
+ *                       and writes one partial output with its log-sum-exp
+ *                       per descriptor.
+ *   3. hpcattn_combine  per layer: merge each (request, KV head)'s partials
+ *                       under the global softmax.
+ *   hpcattn_static_decode is the static split-KV scheme the pages compare
+ *   against (fixed split count, or fixed chunk size), for ablation.
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument is a DEVICE pointer unless marked "host".
+ *   - The caller owns every buffer.  The library allocates, frees and caches
+ *     nothing, keeps no global state, never synchronises and never copies
+ *     between host and device.  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL is the default stream) and is safe to capture in a HIP graph.
+ *   - Return 0 (HPCATTN_OK) or a negative hpcattn_status.  Argument errors
+ *     are detected on the host before anything is enqueued; a launch error
+ *     reported by the runtime returns HPCATTN_ERR_LAUNCH.
+ *   - Layouts are row-major and contiguous:
+ *       q           [B, H_q, D]              bf16, or e4m3 bytes
+ *       q_scale     [B, H_q]                 fp32 (fp8 only)
+ *       k_pages     [num_pages, H_kv, 64, D] bf16, or e4m3 bytes
+ *       v_pages     [num_pages, H_kv, 64, D] same type as k_pages
+ *       k_scale     [num_pages, H_kv, 64]    fp32 (fp8 only); v_scale likewise
+ *       page_table  [B, max_pages_per_req]   int32; token t of request b sits
+ *                   in slot t % 64 of page page_table[b][t / 64]
+ *       part_o      [max_partials, G, D]     fp32, normalised partial output
+ *       part_lse    [max_partials, G]        fp32, natural-log LSE of the
+ *                   scaled logits of the partial's tokens
+ *       out         [B, H_q, D]              bf16 (round to nearest even)
+ *       out_lse     [B, H_q]                 fp32, natural log
+ *     G = H_q / H_kv; query head j reads KV head j / G.  fp8 is OCP E4M3FN
+ *     and a value is code * scale.
+ *   - Data errors (a length beyond 64 * max_pages_per_req, a page id outside
+ *     [0, num_pages)) never fault: out-of-range tiles are skipped and their
+ *     tokens contribute nothing; plan sets the map's error word.
+ */
+#ifndef HPCATTN_H
+#define HPCATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HPCATTN_PAGE_SIZE 64   /* tokens per KV page and per tile            */
+#define HPCATTN_MAX_BATCH 8192 /* requests per plan                          */
+#define HPCATTN_MAX_GROUP 16   /* query heads per KV head                     */
+
+typedef enum {
+    HPCATTN_OK = 0,
+    HPCATTN_ERR_NULL = -1,      /* a required pointer is NULL                  */
+    HPCATTN_ERR_SHAPE = -2,     /* a size is out of range or inconsistent      */
+    HPCATTN_ERR_DTYPE = -3,     /* unknown dtype, or scales given/missing      */
+    HPCATTN_ERR_WORKSPACE = -4, /* a caller buffer is smaller than required    */
+    HPCATTN_ERR_LAUNCH = -5,    /* the HIP runtime reported a launch error     */
+    HPCATTN_ERR_ARG = -6        /* another argument is out of range            */
+} hpcattn_status;
+
+typedef enum {
+    HPCATTN_KV_BF16 = 0,        /* q, k_pages, v_pages in bf16                 */
+    HPCATTN_KV_FP8_E4M3 = 1     /* OCP E4M3FN bytes with fp32 scales           */
+} hpcattn_kv_dtype;
+
+/* Error word (map header word 7) values written by hpcattn_plan. */
+#define HPCATTN_MAPERR_NEG_LEN 1   /* a sequence length < 0 (taken as 0)      */
+#define HPCATTN_MAPERR_OVERFLOW 2  /* more than 2^31 - 1 tiles in the batch   */
+
+/* Problem shape of one attention layer (host struct). */
+typedef struct {
+    int32_t batch;              /* B >= 1                                      */
+    int32_t num_q_heads;        /* H_q, a multiple of H_kv                     */
+    int32_t num_kv_heads;       /* H_kv >= 1; G = H_q / H_kv <= 16             */
+    int32_t head_dim;           /* D, 64 or 128                                */
+    int32_t max_pages_per_req;  /* columns of page_table                       */
+    int32_t num_pages;          /* pages in k_pages / v_pages                  */
+    int32_t kv_dtype;           /* hpcattn_kv_dtype                            */
+    float sm_scale;             /* softmax scale on q . k, e.g. 1/sqrt(D)      */
+} hpcattn_dims;
+
+/*
+ * Task map handle (host struct describing a device buffer).
+ *
+ * The device buffer holds int32 words:
+ *   [0..7]  header {T, P_eff, q, r, num_desc, B, H_kv, err}
+ *   then    seq_lens[B]                      copy of the planned lengths
+ *           bin_desc_off[P + 1]              descriptors of bin i are
+ *                                            bin_desc_off[i] .. [i + 1] - 1
+ *           seg_desc_off[B * H_kv + 1]       descriptors of segment
+ *                                            s = b * H_kv + h, contiguous
+ *           desc[B * H_kv + P - 1][4]        {b, h, t0, t1}: tiles [t0, t1)
+ *                                            of segment (b, h); unused
+ *                                            entries are zero
+ * T is the total tile count, P_eff the bins in use, and bins 0 .. r - 1 own
+ * q + 1 tiles, bins r .. P_eff - 1 own q, the rest none.  A descriptor's
+ * index is its partial slot in part_o / part_lse.
+ */
+typedef struct {
+    int32_t *words;             /* device, hpcattn_task_map_bytes() bytes      */
+    size_t bytes;               /* size of `words` in bytes                    */
+    int32_t batch;              /* B the map was planned for                   */
+    int32_t num_kv_heads;       /* H_kv                                        */
+    int32_t num_bins;           /* P = num_persistent_wg                       */
+    int32_t min_tiles;          /* minimum-work floor m                        */
+} hpcattn_task_map;
+
+/* Bytes of the task map buffer for (B, H_kv, P); 0 if a size is < 1. */
+size_t hpcattn_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_bins);
+
+/* Partial slots a plan can produce: B * H_kv + P - 1 (part_o / part_lse
+ * leading dimension); 0 if a size is < 1. */
+int64_t hpcattn_max_partials(int32_t batch, int32_t num_kv_heads, int32_t num_bins);
+
+/*
+ * The assign step ("Scheduling around live KV work"; "Attention dynamic
+ * scheduling": the task map is built before each step from device-side
+ * lengths and every layer's attention takes its tasks from it).
+ *
+ * seq_lens   device int32 [batch], live KV tokens per request.
+ * num_bins   P >= 1, the number of persistent workgroups of hpcattn_decode.
+ * min_tiles  m >= 1, minimum-work floor: at most max(1, T / m) bins are used,
+ *            so each used bin owns >= m tiles when T >= m.
+ * map        host struct: in `words`/`bytes` (device buffer, at least
+ *            hpcattn_task_map_bytes(batch, num_kv_heads, num_bins) bytes);
+ *            out: the other fields.  One workgroup of 1024 threads writes the
+ *            whole buffer.  Deterministic: the words are a pure function of
+ *            (seq_lens, num_kv_heads, num_bins, min_tiles).
+ * Errors: NULL pointers, batch outside [1, HPCATTN_MAX_BATCH], H_kv < 1,
+ * P < 1, m < 1, a buffer smaller than required.
+ */
+int hpcattn_plan(const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads,
+                 int32_t num_bins, int32_t min_tiles, hpcattn_task_map *map,
+                 void *stream);
+
+/*
+ * The persistent decode step ("Scheduling around live KV work": each
+ * workgroup drains its bin, computing attention over one or more contiguous
+ * KV tiles per descriptor and writing a partial output with its log-sum-exp).
+ *
+ * Launches map->num_bins workgroups of 256 threads; bin i is drained by
+ * workgroup i.  Writes part_o / part_lse rows 0 .. num_desc - 1 and nothing
+ * else.  dims->batch and dims->num_kv_heads must equal the map's.
+ * q_scale, k_scale, v_scale: NULL for bf16, required for fp8.
+ * part_o / part_lse: at least hpcattn_max_partials(B, H_kv, P) rows;
+ * part_o_rows gives the caller's row capacity.
+ */
+int hpcattn_decode(const hpcattn_dims *dims, const void *q, const float *q_scale,
+                   const void *k_pages, const void *v_pages,
+                   const float *k_scale, const float *v_scale,
+                   const int32_t *page_table, const hpcattn_task_map *map,
+                   float *part_o, float *part_lse, int64_t part_o_rows,
+                   void *stream);
+
+/*
+ * The combine step ("Scheduling around live KV work": a final kernel reads
+ * each request's and head's actual chunk count and merges the partials under
+ * the global softmax normalisation; "Attention dynamic scheduling": the
+ * Combine kernel merges the split-KV results).
+ *
+ * For segment s = (b, h) with partials k in seg_desc_off[s] .. [s + 1] - 1:
+ *   M = max_k lse_k,  w_k = exp(lse_k - M),
+ *   out = sum_k w_k o_k / sum_k w_k,  out_lse = M + ln sum_k w_k.
+ * A request with no live KV gets out = 0 and out_lse = -inf.
+ * out_lse may be NULL.
+ */
+int hpcattn_combine(const hpcattn_dims *dims, const hpcattn_task_map *map,
+                    const float *part_o, const float *part_lse, void *out,
+                    float *out_lse, void *stream);
+
+/*
+ * Static split-KV decode, the scheme the dynamic one replaces ("Attention:
+ * load balancing for variable-length decode": a fixed launch grid over KV
+ * heads, requests and KV chunks with one partition policy for the batch).
+ *
+ * policy 0, fixed split count: param = S >= 1 splits per (request, KV head);
+ *   split k of a request with n tiles owns tiles [k n / S, (k + 1) n / S).
+ * policy 1, fixed chunk size: param = C tokens, a positive multiple of 64;
+ *   the grid reserves ceil(max_seq_len / C) chunks per (request, KV head)
+ *   and chunk k owns tokens [k C, (k + 1) C) clipped to the length.
+ * max_seq_len (host) bounds every seq_lens[b] and sizes the policy-1 grid.
+ * One workgroup of 256 threads per (request, KV head, split); empty splits
+ * write lse = -inf.  Then the combine runs over the fixed splits and writes
+ * out / out_lse like hpcattn_combine.  part_o / part_lse need
+ * hpcattn_static_max_partials() rows (given in part_o_rows).
+ */
+int hpcattn_static_decode(const hpcattn_dims *dims, int32_t policy, int32_t param,
+                          int32_t max_seq_len, const int32_t *seq_lens,
+                          const void *q, const float *q_scale,
+                          const void *k_pages, const void *v_pages,
+                          const float *k_scale, const float *v_scale,
+                          const int32_t *page_table, float *part_o, float *part_lse,
+                          int64_t part_o_rows, void *out, float *out_lse,
+                          void *stream);
+
+/* Partial rows hpcattn_static_decode needs: B * H_kv * splits, where splits
+ * is S (policy 0) or ceil(max_seq_len / C) (policy 1); 0 on bad input. */
+int64_t hpcattn_static_max_partials(int32_t batch, int32_t num_kv_heads, int32_t policy,
+                                    int32_t param, int32_t max_seq_len);
+
+/* Static description of a status code (host string, never NULL). */
+const char *hpcattn_strerror(int status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int hpcattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HPCATTN_H */

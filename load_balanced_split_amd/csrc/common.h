@@ -1,0 +1,69 @@
+// Internal declarations shared by the HIP translation units of libhpcattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hpcattn.h"
+
+namespace hpcattn {
+
+constexpr int kTile = HPCATTN_PAGE_SIZE;  // tokens per tile and per page
+constexpr int kWaves = 4;                 // waves per decode workgroup
+constexpr int kDecodeThreads = 64 * kWaves;
+constexpr int kPlanThreads = 1024;
+
+// Word offsets inside a task map (layout documented in hpcattn.h).
+struct MapLayout {
+    int64_t lens, bin_off, seg_off, desc, words;
+    __host__ __device__ MapLayout(int32_t B, int32_t Hkv, int32_t P) {
+        const int64_t S = (int64_t)B * Hkv;
+        lens = 8;
+        bin_off = lens + B;
+        seg_off = bin_off + (int64_t)P + 1;
+        desc = seg_off + S + 1;
+        words = desc + 4 * (S + P - 1);
+    }
+};
+
+// Arguments of the decode kernels (dynamic and static), passed by value.
+struct DecodeParams {
+    const void *q;
+    const float *q_scale;
+    const void *k;
+    const void *v;
+    const float *k_scale;
+    const float *v_scale;
+    const int32_t *page_table;
+    float *part_o;
+    float *part_lse;
+    // dynamic: task map; static: seq_lens
+    const int32_t *map;
+    const int32_t *seq_lens;
+    int32_t B, Hq, Hkv, G, max_pages, num_pages;
+    int32_t P;              // bins (dynamic)
+    int32_t policy, param;  // static split policy and its parameter
+    int32_t splits;         // static: slots per segment
+    float scale_log2;       // sm_scale * log2(e)
+};
+
+struct CombineParams {
+    const float *part_o;
+    const float *part_lse;
+    const int32_t *seg_off;  // CSR of partial slots per segment, or NULL
+    int32_t stride;          // when seg_off is NULL: segment s owns slots
+                             // [s * stride, (s + 1) * stride)
+    void *out;
+    float *out_lse;
+    int32_t S, G, D;
+};
+
+hipError_t launch_plan(const int32_t *seq_lens, int32_t B, int32_t Hkv, int32_t P,
+                       int32_t m, int32_t *map, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dtype,
+                         hipStream_t stream);
+hipError_t launch_static_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dtype,
+                                hipStream_t stream);
+hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+
+}  // namespace hpcattn

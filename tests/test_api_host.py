@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI: no GPU needed, no kernel is launched.
+
+Every call below fails validation on the host before anything is enqueued,
+so fake (non-NULL) device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hpcattn.h")
+LIB = os.path.join(ROOT, "load_balanced_split_amd", "libhpcattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libhpcattn.so not built")
+
+
+@pytest.fixture(scope="module")
+def H():
+    from load_balanced_split_amd import hpcattn
+    return hpcattn
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hpcattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(H):
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(H.EXPORTS)
+    assert H.hpcattn_version() == 100
+
+
+def test_size_queries_match_layout(H):
+    for B, Hkv, P in [(1, 1, 1), (4, 1, 8), (64, 8, 512), (128, 8, 1024), (3, 2, 7)]:
+        assert H.hpcattn_task_map_bytes(B, Hkv, P) == 4 * oracle.plan_words(B, Hkv, P)
+        assert H.hpcattn_max_partials(B, Hkv, P) == B * Hkv + P - 1
+    assert H.hpcattn_task_map_bytes(0, 1, 1) == 0
+    assert H.hpcattn_max_partials(1, 0, 1) == 0
+    assert H.hpcattn_static_max_partials(4, 2, 0, 8, 1000) == 64
+    assert H.hpcattn_static_max_partials(4, 2, 1, 256, 1000) == 4 * 2 * 4
+    assert H.hpcattn_static_max_partials(4, 2, 1, 100, 1000) == 0     # not a multiple of 64
+    assert H.hpcattn_static_max_partials(4, 2, 2, 8, 1000) == 0       # unknown policy
+
+
+FAKE = 0x10000   # never dereferenced: each call below is rejected first
+
+
+def _map(H, B=4, Hkv=1, P=8, nbytes=None):
+    if nbytes is None:
+        nbytes = H.hpcattn_task_map_bytes(B, Hkv, P)
+    return H.hpcattn_task_map(FAKE, nbytes, B, Hkv, P, 2)
+
+
+def test_plan_rejects_bad_arguments(H):
+    lib = H._lib
+    m = _map(H)
+    assert lib.hpcattn_plan(None, 4, 1, 8, 2, ctypes.byref(m), None) == H.ERR_NULL
+    assert lib.hpcattn_plan(FAKE, 4, 1, 8, 2, None, None) == H.ERR_NULL
+    assert lib.hpcattn_plan(FAKE, 0, 1, 8, 2, ctypes.byref(m), None) == H.ERR_SHAPE
+    assert lib.hpcattn_plan(FAKE, H.MAX_BATCH + 1, 1, 8, 2, ctypes.byref(m), None) == H.ERR_SHAPE
+    assert lib.hpcattn_plan(FAKE, 4, 0, 8, 2, ctypes.byref(m), None) == H.ERR_SHAPE
+    assert lib.hpcattn_plan(FAKE, 4, 1, 0, 2, ctypes.byref(m), None) == H.ERR_SHAPE
+    assert lib.hpcattn_plan(FAKE, 4, 1, 8, 0, ctypes.byref(m), None) == H.ERR_ARG
+    small = _map(H, nbytes=H.hpcattn_task_map_bytes(4, 1, 8) - 4)
+    assert lib.hpcattn_plan(FAKE, 4, 1, 8, 2, ctypes.byref(small), None) == H.ERR_WORKSPACE
+    nowords = H.hpcattn_task_map(None, 1 << 20, 4, 1, 8, 2)
+    assert lib.hpcattn_plan(FAKE, 4, 1, 8, 2, ctypes.byref(nowords), None) == H.ERR_NULL
+
+
+def _dims(H, **kw):
+    d = dict(batch=4, num_q_heads=4, num_kv_heads=1, head_dim=64, max_pages_per_req=16,
+             num_pages=22, kv_dtype=H.KV_BF16, sm_scale=0.125)
+    d.update(kw)
+    return H.hpcattn_dims(**d)
+
+
+def _decode(H, dims, m, q_scale=None, k_scale=None, v_scale=None, rows=1 << 20, part=FAKE,
+            ptrs=FAKE):
+    return H._lib.hpcattn_decode(ctypes.byref(dims) if dims is not None else None, ptrs,
+                                 q_scale, ptrs, ptrs, k_scale, v_scale, ptrs,
+                                 ctypes.byref(m) if m is not None else None, part, part, rows,
+                                 None)
+
+
+def test_decode_rejects_bad_arguments(H):
+    m = _map(H)
+    assert _decode(H, None, m) == H.ERR_NULL
+    assert _decode(H, _dims(H), None) == H.ERR_NULL
+    assert _decode(H, _dims(H), m, ptrs=None) == H.ERR_NULL
+    assert _decode(H, _dims(H), m, part=None) == H.ERR_NULL
+    assert _decode(H, _dims(H, num_q_heads=6, num_kv_heads=4), m) == H.ERR_SHAPE   # H_q % H_kv
+    assert _decode(H, _dims(H, num_q_heads=34, num_kv_heads=2), m) == H.ERR_SHAPE  # G > 16
+    assert _decode(H, _dims(H, head_dim=96), m) == H.ERR_SHAPE
+    assert _decode(H, _dims(H, num_pages=0), m) == H.ERR_SHAPE
+    assert _decode(H, _dims(H, batch=5), m) == H.ERR_SHAPE        # map planned for B = 4
+    assert _decode(H, _dims(H, kv_dtype=7), m) == H.ERR_DTYPE
+    assert _decode(H, _dims(H), m, q_scale=FAKE) == H.ERR_DTYPE   # bf16 with scales
+    assert _decode(H, _dims(H, kv_dtype=H.KV_FP8_E4M3), m, q_scale=FAKE,
+                   k_scale=FAKE) == H.ERR_DTYPE                    # fp8 missing v_scale
+    assert _decode(H, _dims(H, sm_scale=float("nan")), m) == H.ERR_ARG
+    assert _decode(H, _dims(H), m, rows=4 * 1 + 8 - 2) == H.ERR_WORKSPACE
+    small = _map(H, nbytes=16)
+    assert _decode(H, _dims(H), small) == H.ERR_WORKSPACE
+
+
+def test_combine_and_static_reject_bad_arguments(H):
+    lib = H._lib
+    m = _map(H)
+    d = _dims(H)
+    assert lib.hpcattn_combine(ctypes.byref(d), ctypes.byref(m), FAKE, FAKE, None, None,
+                               None) == H.ERR_NULL
+    assert lib.hpcattn_combine(ctypes.byref(_dims(H, batch=3)), ctypes.byref(m), FAKE, FAKE,
+                               FAKE, None, None) == H.ERR_SHAPE
+
+    def st(dims, policy, param, max_len=1000, rows=1 << 20, seq=FAKE):
+        return lib.hpcattn_static_decode(ctypes.byref(dims), policy, param, max_len, seq, FAKE,
+                                         None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, rows,
+                                         FAKE, None, None)
+
+    assert st(d, 2, 8) == H.ERR_ARG
+    assert st(d, 0, 0) == H.ERR_ARG
+    assert st(d, 1, 100) == H.ERR_ARG
+    assert st(d, 1, 256, max_len=-1) == H.ERR_ARG
+    assert st(d, 0, 8, rows=4 * 8 - 1) == H.ERR_WORKSPACE
+    assert st(d, 0, 8, seq=None) == H.ERR_NULL
+    assert st(_dims(H, head_dim=32), 0, 8) == H.ERR_SHAPE
+
+
+def test_strerror_covers_every_status(H):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert H.hpcattn_strerror(code) != "unknown status"
+    assert H.hpcattn_strerror(-99) == "unknown status"
