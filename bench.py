@@ -64,7 +64,46 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="instead of the benchmark: time a plain 1 GiB device copy and a "
+                         "4 GiB read-reduce (HBM read probe), print one JSON line")
     return ap.parse_args()
+
+
+def calibrate():
+    """Reference kernels of known traffic: torch's device copy of 1 GiB (the
+    scale for the HBM byte counters) and a 4 GiB read-reduce (the achievable
+    read bandwidth)."""
+    import torch
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    n_copy = 1 << 30
+    x = torch.zeros(n_copy // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    big = torch.zeros((1 << 32) // 2, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    copy_ms = timed(lambda: y.copy_(x), 5)
+    read_ms = timed(lambda: big.sum(dtype=torch.float32), 5)
+    print(json.dumps({
+        "calibration": "device copy of %d bytes; read-reduce of %d bytes" % (n_copy, big.numel() * 2),
+        "copy_bytes": n_copy, "copy_ms": round(copy_ms, 4),
+        "copy_GBs_read_plus_write": round(2 * n_copy / copy_ms / 1e6, 1),
+        "read_bytes": big.numel() * 2, "read_ms": round(read_ms, 4),
+        "read_GBs": round(big.numel() * 2 / read_ms / 1e6, 1)}), flush=True)
 
 
 def traffic_from_profile():
@@ -83,8 +122,9 @@ def traffic_from_profile():
 
 def cpu_baseline(prob, budget_s: float):
     """The fp64 oracle, as it stands, on all host cores over a bounded sample
-    of layer 0: whole (request, KV head) pairs in a seeded order until the
-    time budget is spent.  Returns the KV GB/s it sustained."""
+    of layer 0: whole (request, KV head) pairs in a seeded order, cycling
+    over the layer, until the time budget is spent.  Returns the KV GB/s it
+    sustained."""
     import numpy as np
 
     import oracle
@@ -103,8 +143,8 @@ def cpu_baseline(prob, budget_s: float):
     cores = oracle.max_threads()
     done_tok, spent, i = 0, 0.0, 0
     chunk = max(cores, 8)
-    while i < len(pairs) and spent < budget_s:
-        sel = pairs[i:i + chunk]
+    while spent < budget_s:
+        sel = [pairs[(i + k) % len(pairs)] for k in range(chunk)]
         t0 = time.perf_counter()
         oracle.attention(h["q"], h["k_pages"], h["v_pages"], h["page_table"], h["seq_lens"],
                          num_kv_heads=w.num_kv_heads, sm_scale=prob.sm_scale,
@@ -116,12 +156,16 @@ def cpu_baseline(prob, budget_s: float):
     per_tok_head = wl.kv_bytes_per_token(w) // w.num_kv_heads
     gbs = done_tok * per_tok_head / spent / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "layer 0, %d of %d (request, KV head) pairs (%d KV tokens), %.1f s of "
-                      "fp64 C/OpenMP work" % (i, len(pairs), done_tok, spent)}
+            "sample": "layer 0 of the same workload, %d (request, KV head) attention tasks "
+                      "(%.2f passes over the layer's %d pairs, %d KV tokens), %.1f s of fp64 "
+                      "C/OpenMP work" % (i, i / len(pairs), len(pairs), done_tok, spent)}
 
 
 def main():
     args = parse_args()
+    if args.calibrate:
+        calibrate()
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
