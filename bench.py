@@ -9,9 +9,12 @@ are resident in HBM before the timed region starts.
                     [--num-bins P] [--min-tiles m] [--ablation] [--no-cpu-baseline]
 
 Prints one JSON line.  `value` is the step's KV-read throughput (live KV
-bytes of all layers / step time); `roofline` is for the decode kernel, timed
-per launch with HIP events on the stream it runs on; `cpu_baseline` is the
-fp64 oracle on the host cores over a bounded sample of the same workload.
+bytes of all layers / step time), the step replayed from a HIP graph as a
+serving loop would (--eager launches each kernel from the host instead);
+`roofline` is for the decode kernel, its average launch time taken with HIP
+events around a graph of back-to-back decode launches on the stream they run
+on; `cpu_baseline` is the fp64 oracle on the host cores over a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
@@ -62,6 +65,9 @@ def parse_args():
     ap.add_argument("--ablation", action="store_true",
                     help="also sweep the static split-KV baseline on the same inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from the host instead of replaying the step "
+                         "from a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate", action="store_true",
@@ -96,14 +102,24 @@ def calibrate():
             ts.append(a.elapsed_time(b))
         return statistics.median(ts)
 
+    from load_balanced_split_amd import hpcattn as H
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     copy_ms = timed(lambda: y.copy_(x), 5)
     read_ms = timed(lambda: big.sum(dtype=torch.float32), 5)
+    probe = {}
+    for nt in (False, True):
+        for wg in (512, 1024, 2048, 4096, 8192, 16384, 32768):
+            ms = timed(lambda: H.hpcattn_probe_stream_read(big, wg, sink, nt), 5)
+            probe["%s%d" % ("nt" if nt else "plain", wg)] = round(big.numel() * 2 / ms / 1e6, 1)
+    best = max(probe, key=probe.get)
     print(json.dumps({
-        "calibration": "device copy of %d bytes; read-reduce of %d bytes" % (n_copy, big.numel() * 2),
+        "calibration": "device copy of %d bytes; read-reduce and stream-read probe of %d bytes"
+                       % (n_copy, big.numel() * 2),
         "copy_bytes": n_copy, "copy_ms": round(copy_ms, 4),
         "copy_GBs_read_plus_write": round(2 * n_copy / copy_ms / 1e6, 1),
-        "read_bytes": big.numel() * 2, "read_ms": round(read_ms, 4),
-        "read_GBs": round(big.numel() * 2 / read_ms / 1e6, 1)}), flush=True)
+        "read_bytes": big.numel() * 2, "torch_sum_GBs": round(big.numel() * 2 / read_ms / 1e6, 1),
+        "stream_read_GBs_by_loads_workgroups": probe, "stream_read_best_GBs": probe[best],
+        "stream_read_best": best}), flush=True)
 
 
 def traffic_from_profile():
@@ -188,54 +204,77 @@ def main():
     live_tokens = int(prob.seq_lens.sum())
     kv_bytes_layer = live_tokens * wl.kv_bytes_per_token(w)
 
-    def step(k, ev=None):
+    def step(k):
+        """One decode step: plan once, then decode + combine per layer."""
         run.plan()
         for layer in range(layers):
-            pool = (k * layers + layer) % pools
-            if ev is not None:
-                ev[layer][0].record(stream)
-            run.decode(pool)
-            if ev is not None:
-                ev[layer][1].record(stream)
+            run.decode((k * layers + layer) % pools)
             run.combine()
+
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def capture(fn):
+        """Capture fn's launches into a HIP graph on torch's capture stream."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def graph_avg_ms(fn, count, reps=5):
+        """Average GPU time of one of the `count` launches fn() enqueues, from
+        HIP events around replays of a graph holding them back to back."""
+        g = capture(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = events()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / (reps * count)
 
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
 
-    step_ms, dec_ms = [], []
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # The timed region: K steps, replayed from a HIP graph (default) or
+    # launched eagerly.  A graph holds `per_graph` consecutive steps so that
+    # the one-layer workloads still rotate over their pools.
+    per_graph = 1 if layers >= pools else pools // layers
+    step_ms = []
     wall0 = time.perf_counter()
-    for k in range(args.steps):
-        s0 = torch.cuda.Event(enable_timing=True)
-        s1 = torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        step(args.warmup + k, ev)
-        s1.record(stream)
-        s1.synchronize()
-        step_ms.append(s0.elapsed_time(s1))
-        dec_ms.extend(e0.elapsed_time(e1) for e0, e1 in ev)
-    torch.cuda.synchronize()
+    if args.eager:
+        for k in range(args.steps):
+            a, b = events()
+            a.record(stream)
+            step(args.warmup + k)
+            b.record(stream)
+            b.synchronize()
+            step_ms.append(a.elapsed_time(b))
+    else:
+        g = capture(lambda: [step(k) for k in range(per_graph)])
+        g.replay()
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.steps // per_graph)):
+            a, b = events()
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            b.synchronize()
+            step_ms.append(a.elapsed_time(b) / per_graph)
     wall = time.perf_counter() - wall0
 
-    # Plan and combine alone, for the breakdown (outside the timed steps).
-    def time_op(fn, reps=20):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / reps
-    plan_ms = time_op(run.plan)
-    combine_ms = time_op(run.combine)
+    # Per-kernel GPU time, each kernel back to back in its own graph.
+    n_dec = max(layers, pools) if name == "mixed" else pools
+    dec_avg = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec)
+    combine_ms = graph_avg_ms(lambda: [run.combine() for _ in range(16)], 16)
+    plan_ms = graph_avg_ms(lambda: [run.plan() for _ in range(16)], 16)
+    torch.cuda.synchronize()
 
     med_step = statistics.median(step_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
     value = kv_bytes_layer * layers / (med_step * 1e-3) / 1e9
     achieved = kv_bytes_layer / (dec_avg * 1e-3) / 1e9
     out = {
@@ -267,6 +306,8 @@ def main():
         "breakdown_us": {"plan": round(plan_ms * 1e3, 2),
                          "decode_avg": round(dec_avg * 1e3, 2),
                          "combine": round(combine_ms * 1e3, 2),
+                         "launch_gaps": round((med_step - plan_ms - layers * (dec_avg + combine_ms))
+                                              * 1e3, 1),
                          "step_min": round(min(step_ms) * 1e3, 1),
                          "step_p90": round(sorted(step_ms)[int(0.9 * (len(step_ms) - 1))] * 1e3, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -274,6 +315,7 @@ def main():
                      "traffic": traffic_from_profile(),
                      "kernel": "decode_kernel (one launch = one layer's live KV)"},
         "wall_s_timed": round(wall, 3),
+        "launch": "eager" if args.eager else "hip_graph (%d step(s) per replay)" % per_graph,
     }
 
     if args.ablation:
@@ -284,22 +326,29 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=10):
+def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8):
     """Time the static split-KV baseline (decode + combine) at every sweep
-    point against dynamic decode + combine on the same pools."""
+    point against dynamic decode + combine on the same pools, each as a HIP
+    graph of `reps` back-to-back calls rotating over the pools."""
     import torch
 
     def timed(fn):
+        fn(0)                       # allocates the sweep point's buffers
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                fn((r + 1) % pools)
+        g.replay()
+        torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        fn(0)
-        torch.cuda.synchronize()
         a.record(stream)
-        for r in range(reps):
-            fn((r + 1) % pools)
+        for _ in range(3):
+            g.replay()
         b.record(stream)
         b.synchronize()
-        return a.elapsed_time(b) / reps * 1e3
+        return a.elapsed_time(b) / (3 * reps) * 1e3
 
     def dyn(pool):
         run.decode(pool)

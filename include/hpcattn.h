@@ -212,6 +212,19 @@ int hpcattn_static_decode(const hpcattn_dims *dims, int32_t policy, int32_t para
 int64_t hpcattn_static_max_partials(int32_t batch, int32_t num_kv_heads, int32_t policy,
                                     int32_t param, int32_t max_seq_len);
 
+/*
+ * Measurement reference, not part of the method: a plain streaming read of
+ * `bytes` (a positive multiple of 16) from device buffer `buf`, 16-byte loads
+ * in a grid-stride loop over `workgroups` workgroups of 256 threads; flags
+ * bit 0 selects nontemporal loads (the form the decode kernel uses for KV),
+ * other bits must be 0.  It writes nothing but (practically never) one word
+ * of `sink` (device, 4 bytes).
+ * Timing it gives the achievable HBM read bandwidth that the decode kernel's
+ * bandwidth is compared with.
+ */
+int hpcattn_probe_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
+                              uint32_t *sink, void *stream);
+
 /* Static description of a status code (host string, never NULL). */
 const char *hpcattn_strerror(int status);
 

@@ -209,6 +209,14 @@ int hpcattn_static_decode(const hpcattn_dims *dims, int32_t policy, int32_t para
     return launch_status(launch_combine(c, (hipStream_t)stream));
 }
 
+int hpcattn_probe_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
+                              uint32_t *sink, void *stream) {
+    if (!buf || !sink) return HPCATTN_ERR_NULL;
+    if (bytes < 16 || bytes % 16 || workgroups < 1 || (flags & ~1)) return HPCATTN_ERR_ARG;
+    return launch_status(
+        launch_stream_read(buf, bytes, workgroups, flags, sink, (hipStream_t)stream));
+}
+
 const char *hpcattn_strerror(int status) {
     switch (status) {
     case HPCATTN_OK: return "ok";

@@ -20,6 +20,7 @@
 //     (r = lane % 16, grp = lane / 16) reads token 16 w + r of K at a d-range
 //     that only has to match Q's, and tokens 16 w + 4 grp + j of V at
 //     d = r * D/16 .. + D/16, repacked to the MFMA operand with v_perm;
+//     these are nontemporal loads, since every KV byte is read once;
 //   * the next tile (across descriptor boundaries) is always in flight while
 //     the current one is computed;
 //   * each wave keeps its own running max / sum / O; the 4 waves are merged
@@ -67,6 +68,14 @@ __device__ __forceinline__ T ldg(const void *base, int64_t byte_off) {
     return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
+// KV is streamed once per layer: nontemporal loads keep it from displacing
+// reusable lines (Q, page ids, the task map) in the caches.
+template <class T>
+__device__ __forceinline__ T ldg_stream(const void *base, int64_t byte_off) {
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off));
+}
+
 // ---------------------------------------------------------------------------
 // Element formats.  Each provides the per-lane register image of one tile's
 // share of K and V, of the descriptor's Q, and the two MFMA operand builders.
@@ -101,15 +110,15 @@ struct Bf16 {
         const int64_t krow = (tile_row + ln.r) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            t.k[ks] = ldg<u32x4>(p.k, (krow + 32 * ks + 8 * ln.grp) * 2);
+            t.k[ks] = ldg_stream<u32x4>(p.k, (krow + 32 * ks + 8 * ln.grp) * 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t off = ((tile_row + 4 * ln.grp + j) * D + ln.r * (D / 16)) * 2;
             if constexpr (VW == 4) {
-                u32x4 x = ldg<u32x4>(p.v, off);
+                u32x4 x = ldg_stream<u32x4>(p.v, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1]; t.v[j][2] = x[2]; t.v[j][3] = x[3];
             } else {
-                u32x2 x = ldg<u32x2>(p.v, off);
+                u32x2 x = ldg_stream<u32x2>(p.v, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1];
             }
         }
@@ -172,20 +181,20 @@ struct Fp8 {
         const int64_t tile_row = ((int64_t)page * p.Hkv + h) * kTile + 16 * ln.w;
         const int64_t krow = (tile_row + ln.r) * D;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) t.k[c] = ldg<u32x4>(p.k, krow + 64 * c + 16 * ln.grp);
+        for (int c = 0; c < NC; ++c) t.k[c] = ldg_stream<u32x4>(p.k, krow + 64 * c + 16 * ln.grp);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t off = (tile_row + 4 * ln.grp + j) * D + ln.r * (D / 16);
             if constexpr (VB == 2) {
-                u32x2 x = ldg<u32x2>(p.v, off);
+                u32x2 x = ldg_stream<u32x2>(p.v, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1];
             } else {
-                t.v[j][0] = ldg<uint32_t>(p.v, off);
+                t.v[j][0] = ldg_stream<uint32_t>(p.v, off);
             }
         }
         const int64_t srow = tile_row + 4 * ln.grp;
-        t.ks = ldg<f32x4>(p.k_scale, srow * 4);
-        t.vs = ldg<f32x4>(p.v_scale, srow * 4);
+        t.ks = ldg_stream<f32x4>(p.k_scale, srow * 4);
+        t.vs = ldg_stream<f32x4>(p.v_scale, srow * 4);
     }
 
     __device__ static f32x4 scores(const DecodeParams &p, const Q &q, const Tile &t,

@@ -72,6 +72,7 @@ _sig = {
     "hpcattn_static_decode": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims), _i32, _i32, _i32,
                                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _i64, _vp, _vp, _vp]),
+    "hpcattn_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _vp, _vp]),
     "hpcattn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "hpcattn_version": (ctypes.c_int, []),
 }
@@ -201,3 +202,12 @@ def hpcattn_static_decode(dims: hpcattn_dims, policy: int, param: int, max_seq_l
                                       _ptr(page_table), _ptr(part_o), _ptr(part_lse), rows,
                                       _ptr(out), _ptr(out_lse), _stream(stream)),
            "hpcattn_static_decode")
+
+
+def hpcattn_probe_stream_read(buf, workgroups: int, sink, nontemporal: bool = False,
+                              stream=None) -> None:
+    """Streaming read of a whole contiguous device tensor (measurement only)."""
+    _check(_lib.hpcattn_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                          workgroups, 1 if nontemporal else 0, _ptr(sink),
+                                          _stream(stream)),
+           "hpcattn_probe_stream_read")
