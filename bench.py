@@ -111,6 +111,10 @@ def calibrate():
         for wg in (512, 1024, 2048, 4096, 8192, 16384, 32768):
             ms = timed(lambda: H.hpcattn_probe_stream_read(big, wg, sink, nt), 5)
             probe["%s%d" % ("nt" if nt else "plain", wg)] = round(big.numel() * 2 / ms / 1e6, 1)
+    chunked = {}
+    for wg in (512, 768, 1024, 1536, 2048, 4096, 8192, 16384):
+        ms = timed(lambda: H.hpcattn_probe_stream_read(big, wg, sink, True, True), 5)
+        chunked["nt_chunk16k_%d" % wg] = round(big.numel() * 2 / ms / 1e6, 1)
     best = max(probe, key=probe.get)
     print(json.dumps({
         "calibration": "device copy of %d bytes; read-reduce and stream-read probe of %d bytes"
@@ -119,7 +123,8 @@ def calibrate():
         "copy_GBs_read_plus_write": round(2 * n_copy / copy_ms / 1e6, 1),
         "read_bytes": big.numel() * 2, "torch_sum_GBs": round(big.numel() * 2 / read_ms / 1e6, 1),
         "stream_read_GBs_by_loads_workgroups": probe, "stream_read_best_GBs": probe[best],
-        "stream_read_best": best}), flush=True)
+        "stream_read_best": best, "chunked_16k_read_GBs_by_workgroups": chunked,
+        "chunked_16k_read_best_GBs": max(chunked.values())}), flush=True)
 
 
 def traffic_from_profile():

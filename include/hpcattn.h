@@ -127,6 +127,16 @@ size_t hpcattn_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_b
 int64_t hpcattn_max_partials(int32_t batch, int32_t num_kv_heads, int32_t num_bins);
 
 /*
+ * The number of decode workgroups that are co-resident on the current device
+ * (compute units x workgroups per CU at the kernel's register and LDS use)
+ * for this head_dim, kv_dtype and group size G: the natural num_bins, one
+ * persistent workgroup per bin with no second round.  A host query (reads
+ * device attributes, enqueues nothing).  Returns > 0, or HPCATTN_ERR_ARG for
+ * an unsupported shape, HPCATTN_ERR_LAUNCH if the runtime cannot answer.
+ */
+int32_t hpcattn_suggest_num_bins(int32_t head_dim, int32_t kv_dtype, int32_t group);
+
+/*
  * The assign step ("Scheduling around live KV work"; "Attention dynamic
  * scheduling": the task map is built before each step from device-side
  * lengths and every layer's attention takes its tasks from it).
@@ -216,8 +226,10 @@ int64_t hpcattn_static_max_partials(int32_t batch, int32_t num_kv_heads, int32_t
  * Measurement reference, not part of the method: a plain streaming read of
  * `bytes` (a positive multiple of 16) from device buffer `buf`, 16-byte loads
  * in a grid-stride loop over `workgroups` workgroups of 256 threads; flags
- * bit 0 selects nontemporal loads (the form the decode kernel uses for KV),
- * other bits must be 0.  It writes nothing but (practically never) one word
+ * bit 0 selects nontemporal loads (the form the decode kernel uses for KV);
+ * bit 1 reads the buffer as 16 KB chunks in a scattered order (the shape of
+ * the decode kernel's shuffled tiles; `bytes` must then be a power-of-two
+ * number of 16 KB chunks); other bits must be 0.  It writes nothing but (practically never) one word
  * of `sink` (device, 4 bytes).
  * Timing it gives the achievable HBM read bandwidth that the decode kernel's
  * bandwidth is compared with.

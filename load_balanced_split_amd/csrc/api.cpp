@@ -164,6 +164,19 @@ int hpcattn_combine(const hpcattn_dims *dims, const hpcattn_task_map *map,
     return launch_status(launch_combine(c, (hipStream_t)stream));
 }
 
+int32_t hpcattn_suggest_num_bins(int32_t head_dim, int32_t kv_dtype, int32_t group) {
+    if ((head_dim != 64 && head_dim != 128) || group < 1 || group > HPCATTN_MAX_GROUP ||
+        (kv_dtype != HPCATTN_KV_BF16 && kv_dtype != HPCATTN_KV_FP8_E4M3))
+        return HPCATTN_ERR_ARG;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return HPCATTN_ERR_LAUNCH;
+    const int32_t per_cu = decode_resident_per_cu(head_dim, kv_dtype, group);
+    if (per_cu < 1 || cus < 1) return HPCATTN_ERR_LAUNCH;
+    return per_cu * cus;
+}
+
 int64_t hpcattn_static_max_partials(int32_t batch, int32_t num_kv_heads, int32_t policy,
                                     int32_t param, int32_t max_seq_len) {
     if (batch < 1 || num_kv_heads < 1) return 0;
@@ -212,7 +225,11 @@ int hpcattn_static_decode(const hpcattn_dims *dims, int32_t policy, int32_t para
 int hpcattn_probe_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
                               uint32_t *sink, void *stream) {
     if (!buf || !sink) return HPCATTN_ERR_NULL;
-    if (bytes < 16 || bytes % 16 || workgroups < 1 || (flags & ~1)) return HPCATTN_ERR_ARG;
+    if (bytes < 16 || bytes % 16 || workgroups < 1 || (flags & ~3)) return HPCATTN_ERR_ARG;
+    if (flags & 2) {   // a power-of-two number of 16 KB chunks
+        const size_t n = bytes / 16384;
+        if (bytes % 16384 || n == 0 || (n & (n - 1))) return HPCATTN_ERR_ARG;
+    }
     return launch_status(
         launch_stream_read(buf, bytes, workgroups, flags, sink, (hipStream_t)stream));
 }

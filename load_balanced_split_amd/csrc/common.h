@@ -65,6 +65,7 @@ hipError_t launch_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dty
 hipError_t launch_static_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dtype,
                                 hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t group);
 hipError_t launch_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
                               uint32_t *sink, hipStream_t stream);
 

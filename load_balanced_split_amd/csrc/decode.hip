@@ -63,17 +63,27 @@ __device__ __forceinline__ uint32_t halves(uint32_t x, uint32_t y) {
     return __builtin_amdgcn_perm(y, x, hi ? 0x07060302u : 0x05040100u);
 }
 
+// Loads at a uniform base plus a 32-bit per-lane byte offset, so that they
+// use the scalar-base addressing form (no 64-bit address per lane).
 template <class T>
-__device__ __forceinline__ T ldg(const void *base, int64_t byte_off) {
-    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+__device__ __forceinline__ T ldg(const void *base, uint32_t off) {
+    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
 }
 
 // KV is streamed once per layer: nontemporal loads keep it from displacing
 // reusable lines (Q, page ids, the task map) in the caches.
 template <class T>
-__device__ __forceinline__ T ldg_stream(const void *base, int64_t byte_off) {
+__device__ __forceinline__ T ldg_stream(const void *base, uint32_t off) {
     return __builtin_nontemporal_load(
-        reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off));
+        reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off));
+}
+
+// Start of the 64-token tile (page, h) of a [num_pages, H_kv, 64, D] pool
+// with `esize`-byte elements (uniform across the workgroup).
+__device__ __forceinline__ const char *tile_base(const void *pool, int page, int h, int Hkv,
+                                                 int row_bytes) {
+    return reinterpret_cast<const char *>(pool) +
+           ((int64_t)page * Hkv + h) * (int64_t)kTile * row_bytes;
 }
 
 // ---------------------------------------------------------------------------
@@ -94,31 +104,31 @@ struct Bf16 {
         u32x4 q[KS];
     };
 
-    __device__ static void load_q(const DecodeParams &p, int b, int h, const Lane &ln, Q &q) {
-        const int g = ln.r;
-        const int64_t row = (int64_t)b * p.Hq + (int64_t)h * p.G + (g < p.G ? g : 0);
+    static constexpr int kQRowBytes = D * 2;
+
+    // The MFMA B-operand image of Q (head g = r, d-range of k-step ks and
+    // lane group grp) from the LDS copy of the group's rows.
+    __device__ static void read_q(const uint32_t *sq, int stride, const Lane &ln, Q &q) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = ldg<u32x4>(p.q, (row * D + 32 * ks + 8 * ln.grp) * 2);
-            q.q[ks] = g < p.G ? x : u32x4{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            q.q[ks] = *reinterpret_cast<const u32x4 *>(sq + ln.r * stride + 16 * ks + 4 * ln.grp);
     }
 
     __device__ static void load_tile(const DecodeParams &p, int page, int h, const Lane &ln,
                                      Tile &t) {
-        const int64_t tile_row = ((int64_t)page * p.Hkv + h) * kTile + 16 * ln.w;
-        const int64_t krow = (tile_row + ln.r) * D;
+        const char *kb = tile_base(p.k, page, h, p.Hkv, D * 2);
+        const char *vb = tile_base(p.v, page, h, p.Hkv, D * 2);
+        const uint32_t koff = ((16 * ln.w + ln.r) * D + 8 * ln.grp) * 2;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            t.k[ks] = ldg_stream<u32x4>(p.k, (krow + 32 * ks + 8 * ln.grp) * 2);
+        for (int ks = 0; ks < KS; ++ks) t.k[ks] = ldg_stream<u32x4>(kb, koff + 64 * ks);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t off = ((tile_row + 4 * ln.grp + j) * D + ln.r * (D / 16)) * 2;
+            const uint32_t off = ((16 * ln.w + 4 * ln.grp + j) * D + ln.r * (D / 16)) * 2;
             if constexpr (VW == 4) {
-                u32x4 x = ldg_stream<u32x4>(p.v, off);
+                u32x4 x = ldg_stream<u32x4>(vb, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1]; t.v[j][2] = x[2]; t.v[j][3] = x[3];
             } else {
-                u32x2 x = ldg_stream<u32x2>(p.v, off);
+                u32x2 x = ldg_stream<u32x2>(vb, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1];
             }
         }
@@ -166,35 +176,35 @@ struct Fp8 {
         u32x4 q[NC];
     };
 
-    __device__ static void load_q(const DecodeParams &p, int b, int h, const Lane &ln, Q &q) {
-        const int g = ln.r;
-        const int64_t row = (int64_t)b * p.Hq + (int64_t)h * p.G + (g < p.G ? g : 0);
+    static constexpr int kQRowBytes = D;
+
+    __device__ static void read_q(const uint32_t *sq, int stride, const Lane &ln, Q &q) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            u32x4 x = ldg<u32x4>(p.q, row * D + 64 * c + 16 * ln.grp);
-            q.q[c] = g < p.G ? x : u32x4{0, 0, 0, 0};
-        }
+        for (int c = 0; c < NC; ++c)
+            q.q[c] = *reinterpret_cast<const u32x4 *>(sq + ln.r * stride + 16 * c + 4 * ln.grp);
     }
 
     __device__ static void load_tile(const DecodeParams &p, int page, int h, const Lane &ln,
                                      Tile &t) {
-        const int64_t tile_row = ((int64_t)page * p.Hkv + h) * kTile + 16 * ln.w;
-        const int64_t krow = (tile_row + ln.r) * D;
+        const char *kb = tile_base(p.k, page, h, p.Hkv, D);
+        const char *vb = tile_base(p.v, page, h, p.Hkv, D);
+        const uint32_t koff = (16 * ln.w + ln.r) * D + 16 * ln.grp;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) t.k[c] = ldg_stream<u32x4>(p.k, krow + 64 * c + 16 * ln.grp);
+        for (int c = 0; c < NC; ++c) t.k[c] = ldg_stream<u32x4>(kb, koff + 64 * c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t off = (tile_row + 4 * ln.grp + j) * D + ln.r * (D / 16);
+            const uint32_t off = (16 * ln.w + 4 * ln.grp + j) * D + ln.r * (D / 16);
             if constexpr (VB == 2) {
-                u32x2 x = ldg_stream<u32x2>(p.v, off);
+                u32x2 x = ldg_stream<u32x2>(vb, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1];
             } else {
-                t.v[j][0] = ldg_stream<uint32_t>(p.v, off);
+                t.v[j][0] = ldg_stream<uint32_t>(vb, off);
             }
         }
-        const int64_t srow = tile_row + 4 * ln.grp;
-        t.ks = ldg_stream<f32x4>(p.k_scale, srow * 4);
-        t.vs = ldg_stream<f32x4>(p.v_scale, srow * 4);
+        // Scales of tokens 16 w + 4 grp + i: one 16-byte run per lane group.
+        const uint32_t soff = (16 * ln.w + 4 * ln.grp) * 4;
+        t.ks = ldg_stream<f32x4>(tile_base(p.k_scale, page, h, p.Hkv, 4), soff);
+        t.vs = ldg_stream<f32x4>(tile_base(p.v_scale, page, h, p.Hkv, 4), soff);
     }
 
     __device__ static f32x4 scores(const DecodeParams &p, const Q &q, const Tile &t,
@@ -248,9 +258,11 @@ struct State {
 
 // One tile's share for this wave: nv = live tokens of the tile (0 .. 64).
 template <class KV, int D>
-__device__ __forceinline__ void attend_tile(const DecodeParams &p, const typename KV::Q &q,
+__device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_t *sq,
                                             float qs, const typename KV::Tile &t, int nv,
                                             State<D> &st, const Lane &ln) {
+    typename KV::Q q;
+    KV::read_q(sq, KV::kQRowBytes / 4 + 4, ln, q);
     f32x4 s = KV::scores(p, q, t, qs, 0, 0, ln);
     const int tok0 = 16 * ln.w + 4 * ln.grp;
     if (nv < kTile) {
@@ -304,12 +316,28 @@ struct MergeLds {
     float o[kWaves][GR][D];
     float m[kWaves][GR];
     float l[kWaves][GR];
+    // The current descriptor's Q rows (16 rows, rows >= G zero), each padded
+    // by 4 dwords so that the per-tile operand reads are bank-conflict free.
+    uint32_t q[16 * (D / 2 + 4)];
 };
 
+// Copy the G query rows of (b, h) into the LDS Q rows.  All threads.
+template <class KV, int D, int GR>
+__device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR> &sm, int b,
+                                        int h) {
+    constexpr int RW = KV::kQRowBytes / 4, QS = RW + 4;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(
+        reinterpret_cast<const char *>(p.q) +
+        ((int64_t)b * p.Hq + (int64_t)h * p.G) * KV::kQRowBytes);
+    for (int i = threadIdx.x; i < p.G * RW; i += kDecodeThreads)
+        sm.q[(i / RW) * QS + i % RW] = src[i];
+}
+
 // Merge the waves' states and write partial slot `slot`.  All threads.
-template <int D, int GR>
-__device__ void merge_write(const DecodeParams &p, State<D> &st, MergeLds<D, GR> &sm,
-                            int64_t slot, const Lane &ln) {
+template <int D, int GR, class Between>
+__device__ __forceinline__ void merge_write(const DecodeParams &p, State<D> &st,
+                                            MergeLds<D, GR> &sm, int64_t slot, const Lane &ln,
+                                            Between between) {
     const int G = p.G;
     if (ln.r < G) {
         if (ln.grp == 0) {
@@ -347,6 +375,7 @@ __device__ void merge_write(const DecodeParams &p, State<D> &st, MergeLds<D, GR>
             p.part_lse[slot * G + g] =
                 M == kNegInf ? kNegInf : (M + log2f(wsum)) * kLn2;
     }
+    between();   // e.g. stage the next descriptor's Q: no wave reads it now
     __syncthreads();
 }
 
@@ -359,27 +388,45 @@ struct Pos {
     int b, h, t, t1, L;
 };
 
-// Descriptor sources: the task map's bin (dynamic) or one fixed split (static).
+// Wave-uniform by construction (same address for every lane): keep it in a
+// scalar register so tile bases use the scalar-base load form.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Field-wise select (a whole-struct ?: would be lowered through memory).
+__device__ __forceinline__ Pos pick(bool c, const Pos &a, const Pos &b) {
+    return Pos{c ? a.d : b.d, c ? a.b : b.b, c ? a.h : b.h,
+               c ? a.t : b.t, c ? a.t1 : b.t1, c ? a.L : b.L};
+}
+
+// Descriptors of a bin in the task map.
 struct MapSource {
     const int32_t *desc;
     const int32_t *lens;
-    int d_end;
-    __device__ void read(const DecodeParams &, int d, Pos &x) const {
+    __device__ __forceinline__ Pos read(int d) const {
         const int32_t *q = desc + 4 * (int64_t)d;
-        x.d = d;
-        x.b = q[0];
-        x.h = q[1];
-        x.t = q[2];
-        x.t1 = q[3];
-        x.L = lens[x.b];
+        const int b = uniform(q[0]);
+        return Pos{d, b, uniform(q[1]), uniform(q[2]), uniform(q[3]), uniform(lens[b])};
     }
 };
+
+// y = the tile after x in drain order; false at the end of the run
+// (descriptors x.d + 1 .. d_end - 1 come from src).  y is written once, from
+// SSA values, so that the position stays in registers.
+__device__ __forceinline__ bool advance(const MapSource &src, int d_end, const Pos &x, Pos &y) {
+    const bool same = x.t + 1 < x.t1;
+    const bool next = !same && x.d + 1 < d_end;
+    Pos n = x;
+    n.t = x.t + 1;
+    if (next) n = src.read(x.d + 1);
+    y = n;
+    return same || next;
+}
 
 // Page id and live-token count of the tile at x; a tile outside the page
 // table or with a page id outside the pool reads page 0 and counts no token.
 __device__ __forceinline__ int locate(const DecodeParams &p, const Pos &x, int &nv) {
     nv = min(kTile, x.L - kTile * x.t);
-    int page = x.t < p.max_pages ? p.page_table[(int64_t)x.b * p.max_pages + x.t] : -1;
+    int page = x.t < p.max_pages ? uniform(p.page_table[(int64_t)x.b * p.max_pages + x.t]) : -1;
     if ((unsigned)page >= (unsigned)p.num_pages) {
         page = 0;
         nv = 0;
@@ -387,81 +434,73 @@ __device__ __forceinline__ int locate(const DecodeParams &p, const Pos &x, int &
     return page;
 }
 
+// fp8: the q_scale of head g = r of (x.b, x.h); 1 for bf16.
+template <class KV>
+__device__ __forceinline__ float q_scale_of(const DecodeParams &p, const Pos &x, const Lane &ln) {
+    if constexpr (KV::kScaled) {
+        const int g = ln.r < p.G ? ln.r : 0;
+        return p.q_scale[(int64_t)x.b * p.Hq + (int64_t)x.h * p.G + g];
+    } else {
+        return 1.f;
+    }
+}
+
+// Drains a run of descriptors tile by tile: while tile i is computed, tile
+// i + 1 (across descriptor boundaries) is being loaded into the other
+// register buffer.  The run starts at `first` and ends with descriptor
+// d_end - 1; partials go to slot d (by_desc) or to slot_base.
 template <class KV, int D, int GR>
-struct Drain {
-    const DecodeParams &p;
-    MergeLds<D, GR> &sm;
-    Lane ln;
-    typename KV::Q q;
-    float qs;
+__device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR> &sm,
+                                      const MapSource &src, const Pos &first, int d_end,
+                                      int64_t slot_base, bool by_desc) {
+    using Tile = typename KV::Tile;
+    const Lane ln;
     State<D> st;
-    Pos cur;
+    Pos cur = first;
     int nv_cur;
-    int d_end;
-    const MapSource *src;
 
-    __device__ Drain(const DecodeParams &p_, MergeLds<D, GR> &sm_) : p(p_), sm(sm_) {}
+    // Q rows past G stay zero for the whole kernel.
+    for (int i = threadIdx.x; i < 16 * (D / 2 + 4); i += kDecodeThreads) sm.q[i] = 0u;
+    __syncthreads();
+    stage_q<KV, D, GR>(p, sm, cur.b, cur.h);
+    float qs = q_scale_of<KV>(p, cur, ln);
+    st.reset();
+    Tile ta, tb;
+    const int pg = locate(p, cur, nv_cur);
+    KV::load_tile(p, pg, cur.h, ln, ta);
+    __syncthreads();
 
-    __device__ void begin_desc() {
-        KV::load_q(p, cur.b, cur.h, ln, q);
-        if constexpr (KV::kScaled) {
-            const int g = ln.r < p.G ? ln.r : 0;
-            qs = p.q_scale[(int64_t)cur.b * p.Hq + (int64_t)cur.h * p.G + g];
-        } else {
-            qs = 1.f;
-        }
-        st.reset();
-    }
-
-    // Issue the next tile's loads into `nxt`, compute the current tile from
-    // `now`, and close the descriptor if it ends.  Returns false when done.
-    __device__ __forceinline__ bool step(typename KV::Tile &now, typename KV::Tile &nxt,
-                                         int64_t slot_base, bool by_desc) {
-        Pos n = cur;
-        bool more = true;
-        if (cur.t + 1 < cur.t1) {
-            n.t = cur.t + 1;
-        } else if (cur.d + 1 < d_end) {
-            src->read(p, cur.d + 1, n);
-        } else {
-            more = false;
-        }
+    // Issue tile i + 1 into `nxt` (after the last tile, a repeat of it that
+    // keeps the steady-state path branch-free), compute tile i from `now`,
+    // close its descriptor if it ends, staging the next descriptor's Q in
+    // LDS inside the merge's barriers.
+    auto step = [&](Tile &now, Tile &nxt) __attribute__((always_inline)) -> bool {
+        Pos n;
+        const bool more = advance(src, d_end, cur, n);
+        const Pos far = pick(more, n, cur);
         int nv_n;
-        const int pg_n = locate(p, more ? n : cur, nv_n);
-        KV::load_tile(p, pg_n, more ? n.h : cur.h, ln, nxt);
+        const int pg_n = locate(p, far, nv_n);
+        KV::load_tile(p, pg_n, far.h, ln, nxt);
 
-        attend_tile<KV, D>(p, q, qs, now, nv_cur, st, ln);
+        attend_tile<KV, D>(p, sm.q, qs, now, nv_cur, st, ln);
 
-        const bool closes = !more || n.d != cur.d;
-        if (closes) {
-            merge_write<D, GR>(p, st, sm, by_desc ? (int64_t)cur.d : slot_base, ln);
-            if (more) {
-                cur = n;
-                begin_desc();
-            }
-        } else {
-            cur = n;
+        if (!more || n.d != cur.d) {
+            merge_write<D, GR>(p, st, sm, by_desc ? (int64_t)cur.d : slot_base, ln, [&] {
+                if (more) stage_q<KV, D, GR>(p, sm, n.b, n.h);
+            });
+            if (!more) return false;
+            qs = q_scale_of<KV>(p, n, ln);
+            st.reset();
         }
+        cur = n;
         nv_cur = nv_n;
-        return more;
+        return true;
+    };
+    while (true) {
+        if (!step(ta, tb)) break;
+        if (!step(tb, ta)) break;
     }
-
-    // Drain descriptors [d_begin, d_end) of src.
-    __device__ void run(const MapSource &s, int d_begin, int d_end_, int64_t slot_base,
-                        bool by_desc) {
-        src = &s;
-        d_end = d_end_;
-        s.read(p, d_begin, cur);
-        typename KV::Tile ta, tb;
-        const int pg = locate(p, cur, nv_cur);
-        KV::load_tile(p, pg, cur.h, ln, ta);
-        begin_desc();
-        while (true) {
-            if (!step(ta, tb, slot_base, by_desc)) break;
-            if (!step(tb, ta, slot_base, by_desc)) break;
-        }
-    }
-};
+}
 
 template <class KV, int D, int GR>
 __global__ void __launch_bounds__(kDecodeThreads)
@@ -469,11 +508,10 @@ decode_kernel(DecodeParams p) {
     __shared__ MergeLds<D, GR> sm;
     const MapLayout lay(p.B, p.Hkv, p.P);
     const int32_t *bin_off = p.map + lay.bin_off;
-    const int d0 = bin_off[blockIdx.x], d1 = bin_off[blockIdx.x + 1];
+    const int d0 = uniform(bin_off[blockIdx.x]), d1 = uniform(bin_off[blockIdx.x + 1]);
     if (d0 >= d1) return;
-    MapSource src{p.map + lay.desc, p.map + lay.lens, d1};
-    Drain<KV, D, GR> dr(p, sm);
-    dr.run(src, d0, d1, 0, true);
+    const MapSource src{p.map + lay.desc, p.map + lay.lens};
+    drain<KV, D, GR>(p, sm, src, src.read(d0), d1, 0, true);
 }
 
 template <class KV, int D, int GR>
@@ -500,19 +538,9 @@ static_decode_kernel(DecodeParams p) {
         return;
     }
     // The same drain as the dynamic kernel, over one range and no map: with
-    // d_end = cur.d + 1 the loop never reads a next descriptor.
-    Drain<KV, D, GR> dr(p, sm);
-    dr.src = nullptr;
-    dr.d_end = 1;
-    dr.cur = Pos{0, b, h, (int)t0, (int)t1, L};
-    typename KV::Tile ta, tb;
-    const int pg = locate(p, dr.cur, dr.nv_cur);
-    KV::load_tile(p, pg, h, dr.ln, ta);
-    dr.begin_desc();
-    while (true) {
-        if (!dr.step(ta, tb, slot, false)) break;
-        if (!dr.step(tb, ta, slot, false)) break;
-    }
+    // d_end = 1 and the range numbered 0 it never reads a descriptor.
+    drain<KV, D, GR>(p, sm, MapSource{nullptr, nullptr}, Pos{0, b, h, (int)t0, (int)t1, L}, 1,
+                     slot, false);
 }
 
 template <template <int> class KV, int D>
@@ -546,6 +574,25 @@ hipError_t dispatch(const DecodeParams &p, int head_dim, int kv_dtype, hipStream
 }
 
 }  // namespace
+
+int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t group) {
+    int n = 0;
+    const void *fn;
+    const bool small = group <= 8;
+    if (kv_dtype == HPCATTN_KV_BF16)
+        fn = head_dim == 128 ? (small ? (const void *)decode_kernel<Bf16<128>, 128, 8>
+                                      : (const void *)decode_kernel<Bf16<128>, 128, 16>)
+                             : (small ? (const void *)decode_kernel<Bf16<64>, 64, 8>
+                                      : (const void *)decode_kernel<Bf16<64>, 64, 16>);
+    else
+        fn = head_dim == 128 ? (small ? (const void *)decode_kernel<Fp8<128>, 128, 8>
+                                      : (const void *)decode_kernel<Fp8<128>, 128, 16>)
+                             : (small ? (const void *)decode_kernel<Fp8<64>, 64, 8>
+                                      : (const void *)decode_kernel<Fp8<64>, 64, 16>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kDecodeThreads, 0) != hipSuccess)
+        return 0;
+    return n;
+}
 
 hipError_t launch_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dtype,
                          hipStream_t stream) {

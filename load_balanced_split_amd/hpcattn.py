@@ -61,6 +61,7 @@ _sig = {
     "hpcattn_task_map_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
     "hpcattn_max_partials": (_i64, [_i32, _i32, _i32]),
     "hpcattn_static_max_partials": (_i64, [_i32, _i32, _i32, _i32, _i32]),
+    "hpcattn_suggest_num_bins": (_i32, [_i32, _i32, _i32]),
     "hpcattn_plan": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32,
                                     ctypes.POINTER(hpcattn_task_map), _vp]),
     "hpcattn_decode": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims), _vp, _vp, _vp, _vp, _vp,
@@ -148,6 +149,13 @@ def hpcattn_static_max_partials(batch, num_kv_heads, policy, param, max_seq_len)
     return int(_lib.hpcattn_static_max_partials(batch, num_kv_heads, policy, param, max_seq_len))
 
 
+def hpcattn_suggest_num_bins(head_dim: int, kv_dtype: int, group: int) -> int:
+    """Co-resident decode workgroups on the current device (needs a GPU)."""
+    n = int(_lib.hpcattn_suggest_num_bins(head_dim, kv_dtype, group))
+    _check(min(n, 0), "hpcattn_suggest_num_bins")
+    return n
+
+
 def hpcattn_strerror(status: int) -> str:
     return _lib.hpcattn_strerror(status).decode()
 
@@ -205,9 +213,10 @@ def hpcattn_static_decode(dims: hpcattn_dims, policy: int, param: int, max_seq_l
 
 
 def hpcattn_probe_stream_read(buf, workgroups: int, sink, nontemporal: bool = False,
-                              stream=None) -> None:
-    """Streaming read of a whole contiguous device tensor (measurement only)."""
+                              chunked: bool = False, stream=None) -> None:
+    """Streaming read of a whole contiguous device tensor (measurement only);
+    `chunked` reads it as scattered 16 KB chunks."""
+    flags = (1 if nontemporal else 0) | (2 if chunked else 0)
     _check(_lib.hpcattn_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
-                                          workgroups, 1 if nontemporal else 0, _ptr(sink),
-                                          _stream(stream)),
+                                          workgroups, flags, _ptr(sink), _stream(stream)),
            "hpcattn_probe_stream_read")

@@ -21,12 +21,17 @@ class DecodeRunner:
         w = prob.workload
         self.prob = prob
         self.device = device
-        self.num_bins = w.num_bins if num_bins is None else num_bins
-        self.min_tiles = w.min_tiles if min_tiles is None else min_tiles
         B = prob.seq_lens.shape[0]
         self.B, self.Hq, self.Hkv, self.D = B, w.num_q_heads, w.num_kv_heads, w.head_dim
         self.G = self.Hq // self.Hkv
         self.fp8 = w.kv_dtype == "fp8"
+        if num_bins is None:
+            num_bins = w.num_bins
+        if num_bins is None:
+            num_bins = H.hpcattn_suggest_num_bins(self.D, H.KV_FP8_E4M3 if self.fp8 else H.KV_BF16,
+                                                  self.G)
+        self.num_bins = num_bins
+        self.min_tiles = w.min_tiles if min_tiles is None else min_tiles
         self.dims = H.make_dims(B, self.Hq, self.Hkv, self.D, prob.page_table.shape[1],
                                 prob.num_pages, H.KV_FP8_E4M3 if self.fp8 else H.KV_BF16,
                                 prob.sm_scale)

@@ -66,8 +66,9 @@ class Workload:
     head_dim: int
     kv_dtype: str            # "bf16" or "fp8"
     layers: int = 1          # distinct KV pools per step
-    num_bins: int = 512      # persistent workgroups (one bin each)
-    min_tiles: int = 4       # minimum-work floor, tiles per bin
+    num_bins: Optional[int] = None  # persistent workgroups (one bin each); None: as many
+                                    # as the device holds at once
+    min_tiles: int = 32      # minimum-work floor, tiles per bin
 
     @property
     def group(self) -> int:

@@ -136,6 +136,18 @@ def test_combine_and_static_reject_bad_arguments(H):
     assert st(_dims(H, head_dim=32), 0, 8) == H.ERR_SHAPE
 
 
+def test_suggest_and_probe_reject_bad_arguments(H):
+    lib = H._lib
+    assert lib.hpcattn_suggest_num_bins(96, H.KV_BF16, 8) == H.ERR_ARG
+    assert lib.hpcattn_suggest_num_bins(128, 5, 8) == H.ERR_ARG
+    assert lib.hpcattn_suggest_num_bins(128, H.KV_BF16, 17) == H.ERR_ARG
+    assert lib.hpcattn_probe_stream_read(None, 1024, 8, 0, FAKE, None) == H.ERR_NULL
+    assert lib.hpcattn_probe_stream_read(FAKE, 1000, 8, 0, FAKE, None) == H.ERR_ARG
+    assert lib.hpcattn_probe_stream_read(FAKE, 1024, 0, 0, FAKE, None) == H.ERR_ARG
+    assert lib.hpcattn_probe_stream_read(FAKE, 1024, 8, 4, FAKE, None) == H.ERR_ARG
+    assert lib.hpcattn_probe_stream_read(FAKE, 3 * 16384, 8, 2, FAKE, None) == H.ERR_ARG
+
+
 def test_strerror_covers_every_status(H):
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert H.hpcattn_strerror(code) != "unknown status"
