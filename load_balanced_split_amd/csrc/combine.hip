@@ -11,48 +11,50 @@
 //   M = max_k lse_k,  w_k = exp(lse_k - M),
 //   out = sum_k w_k o_k / sum_k w_k,  out_lse = M + ln sum_k w_k.
 //
-// One workgroup of 256 threads per (segment, query head of its group).
-// Pass 1 reduces M and sum w over the chunks' LSEs; pass 2 streams the
-// normalised partial rows with float4 loads, D/4 threads per row and
-// 256 / (D/4) rows in flight per round, then reduces the rows in LDS.
+// One workgroup of 4 waves per (segment, query head of its group).  Wave w
+// merges chunks w, w + 4, ... in one pass with a running maximum (each lane
+// owns D/64 consecutive elements of the row, so a chunk's row is one
+// coalesced 512-byte read), four chunks' loads in flight per wave; the four
+// waves are then merged in LDS.  A chunk with lse = -inf (an empty static
+// split) carries no weight and its row is never read.
 #include "common.h"
 
 namespace hpcattn {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 4;
 constexpr float kNegInf = -__builtin_inff();
 
-__device__ float block_reduce(float v, bool is_max, float *s_red) {
+// Running log-sum-exp merge state of one wave lane: max M, weight sum W and
+// the weighted row `acc` (both relative to M).
+template <int E>
+struct Merge {
+    float M = kNegInf, W = 0.f;
+    float acc[E] = {};
+    __device__ void add(float l, const float (&o)[E]) {
+        if (l == kNegInf) return;
+        const float M2 = fmaxf(M, l);
+        const float a = __expf(M - M2), c = __expf(l - M2);   // M = -inf gives a = 0
+        W = W * a + c;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float x = __shfl_xor(v, o, 64);
-        v = is_max ? fmaxf(v, x) : v + x;
+        for (int e = 0; e < E; ++e) acc[e] = acc[e] * a + c * o[e];
+        M = M2;
     }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) s_red[w] = v;
-    __syncthreads();
-    float r = s_red[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) r = is_max ? fmaxf(r, s_red[i]) : r + s_red[i];
-    __syncthreads();
-    return r;
-}
+};
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
-    constexpr int kRowThreads = D / 4;                 // float4 per partial row
-    constexpr int kRows = kThreads / kRowThreads;      // rows per round
-    __shared__ float s_red[kThreads / 64];
-    __shared__ f32x4 s_acc[kRows][kRowThreads];
+    constexpr int E = D / 64;   // elements per lane
+    __shared__ float s_m[kWaves], s_w[kWaves];
+    __shared__ float s_acc[kWaves][D];
 
     const int64_t s = blockIdx.x;
     const int g = blockIdx.y;
     const int G = p.G;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     int64_t k0, k1;
     if (p.seg_off) {
         k0 = p.seg_off[s];
@@ -63,42 +65,54 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
     }
     const int64_t n = k1 - k0;
 
-    float mx = kNegInf;
-    for (int64_t k = threadIdx.x; k < n; k += kThreads) mx = fmaxf(mx, p.part_lse[(k0 + k) * G + g]);
-    const float M = block_reduce(mx, true, s_red);
+    Merge<E> mg;
+    for (int64_t k = w; k < n; k += kWaves * kUnroll) {
+        float l[kUnroll];
+        float o[kUnroll][E];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t kk = k + u * kWaves;
+            const int64_t row = (k0 + (kk < n ? kk : k)) * G + g;
+            l[u] = kk < n ? p.part_lse[row] : kNegInf;
+            const float *src = p.part_o + row * D + lane * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[u][e] = l[u] == kNegInf ? 0.f : src[e];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) mg.add(l[u], o[u]);
+    }
+    if (lane == 0) {
+        s_m[w] = mg.M;
+        s_w[w] = mg.W;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) s_acc[w][lane * E + e] = mg.acc[e];
+    __syncthreads();
+    if (w != 0) return;
+
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i]);
     const int64_t out_row = s * G + g;
-    bf16x2 *out = reinterpret_cast<bf16x2 *>(reinterpret_cast<__bf16 *>(p.out) + out_row * D);
+    __bf16 *out = reinterpret_cast<__bf16 *>(p.out) + out_row * D + lane * E;
     if (M == kNegInf) {   // no live KV: out = 0, lse = -inf
-        for (int i = threadIdx.x; i < D / 2; i += kThreads) out[i] = bf16x2{(__bf16)0.f, (__bf16)0.f};
-        if (p.out_lse && threadIdx.x == 0) p.out_lse[out_row] = kNegInf;
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = (__bf16)0.f;
+        if (p.out_lse && lane == 0) p.out_lse[out_row] = kNegInf;
         return;
     }
-    float ws = 0.f;
-    for (int64_t k = threadIdx.x; k < n; k += kThreads) {
-        const float l = p.part_lse[(k0 + k) * G + g];
-        ws += l == kNegInf ? 0.f : __expf(l - M);
+    float W = 0.f, acc[E] = {};
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const float c = s_m[i] == kNegInf ? 0.f : __expf(s_m[i] - M);
+        W += c * s_w[i];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += c * s_acc[i][lane * E + e];
     }
-    const float wsum = block_reduce(ws, false, s_red);
-
-    const int row = threadIdx.x / kRowThreads, c4 = threadIdx.x % kRowThreads;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int64_t k = row;
-#pragma unroll 4
-    for (; k < n; k += kRows) {
-        const float l = p.part_lse[(k0 + k) * G + g];
-        if (l == kNegInf) continue;   // an empty split: no weight, row never written
-        const f32x4 o = *reinterpret_cast<const f32x4 *>(p.part_o + ((k0 + k) * G + g) * D + 4 * c4);
-        acc += __expf(l - M) * o;
-    }
-    s_acc[row][c4] = acc;
-    __syncthreads();
-    if (row == 0) {
-        for (int i = 1; i < kRows; ++i) acc += s_acc[i][c4];
-        acc = acc * (1.0f / wsum);
-        out[2 * c4] = bf16x2{(__bf16)acc[0], (__bf16)acc[1]};
-        out[2 * c4 + 1] = bf16x2{(__bf16)acc[2], (__bf16)acc[3]};
-        if (p.out_lse && c4 == 0) p.out_lse[out_row] = M + __logf(wsum);
-    }
+    const float inv = 1.0f / W;
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = (__bf16)(acc[e] * inv);
+    if (p.out_lse && lane == 0) p.out_lse[out_row] = M + __logf(W);
 }
 
 }  // namespace
