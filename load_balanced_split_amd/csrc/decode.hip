@@ -41,6 +41,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+// Headroom of the softmax reference max, in log2 units: unnormalised weights
+// are at most 2^8, far inside bf16 and fp32 range.
+constexpr float kSlack = 8.0f;
 
 struct Lane {
     int w, lane, r, grp;
@@ -273,17 +276,27 @@ __device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(st.m, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+    // The reference max st.m moves only when a tile's max exceeds it by more
+    // than kSlack (log2 units), so weights stay <= 2^kSlack and O, l are
+    // rescaled (a wave-uniform branch) only on those rare tiles.
+    if (__any(mx > st.m + kSlack)) {
+        const bool moves = mx > st.m + kSlack;
+        const float m_new = moves ? mx : st.m;
+        // 1 where the reference is kept (also when it stays -inf), 0 from -inf
+        const float alpha = moves ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+        st.l *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 16; ++b) st.o[b] = st.o[b] * alpha;
+        st.m = m_new;
+    }
+    const float m_use = st.m == kNegInf ? 0.f : st.m;
     f32x4 pr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
     float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
-    st.l = st.l * alpha + ps;
-    st.m = m_new;
+    st.l += ps;
 
     if constexpr (KV::kScaled) pr = pr * t.vs;   // fold the per-token V scale into P
     const s16x4 pb = __builtin_bit_cast(
@@ -304,9 +317,9 @@ __device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_
         const u32x2 lo = {halves<false>(vv[0][c], vv[1][c]), halves<false>(vv[2][c], vv[3][c])};
         const u32x2 hi = {halves<true>(vv[0][c], vv[1][c]), halves<true>(vv[2][c], vv[3][c])};
         st.o[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(s16x4, lo), pb, st.o[2 * c] * alpha, 0, 0, 0);
+            __builtin_bit_cast(s16x4, lo), pb, st.o[2 * c], 0, 0, 0);
         st.o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(s16x4, hi), pb, st.o[2 * c + 1] * alpha, 0, 0, 0);
+            __builtin_bit_cast(s16x4, hi), pb, st.o[2 * c + 1], 0, 0, 0);
     }
 }
 
@@ -502,8 +515,10 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR> &sm
     }
 }
 
+// Three workgroups per CU (12 waves) keep enough KV loads in flight; the
+// kernel is written to fit the 168 registers per lane that allows.
 template <class KV, int D, int GR>
-__global__ void __launch_bounds__(kDecodeThreads)
+__global__ void __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(3)))
 decode_kernel(DecodeParams p) {
     __shared__ MergeLds<D, GR> sm;
     const MapLayout lay(p.B, p.Hkv, p.P);
