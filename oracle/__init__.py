@@ -96,6 +96,11 @@ def _load():
             lib.orc_max_threads.restype = i32
             lib.orc_set_threads.argtypes = [i32]
             lib.orc_set_threads.restype = None
+            lib.orc_e4m3_encode.argtypes = [f64]
+            lib.orc_e4m3_encode.restype = i32
+            lib.orc_prologue.argtypes = [i32, i32, i32, i32, P, P, P, P, f64, i32, f64, i32,
+                                         P, P, P, P, P, P, P, P, P]
+            lib.orc_prologue.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -272,3 +277,39 @@ def max_threads() -> int:
 
 def set_threads(n: int) -> None:
     _load().orc_set_threads(int(n))
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest OCP E4M3FN code (ties to even, saturating at +-448)."""
+    return int(_load().orc_e4m3_encode(float(v)))
+
+
+def prologue(qkv, positions, *, num_q_heads, num_kv_heads, head_dim, q_norm_w=None,
+             k_norm_w=None, eps=1e-6, rope=True, rope_base=10000.0, hadamard=False):
+    """The attention prologue for T tokens (qkv: uint16 bf16 bits
+    [T, (H_q + 2 H_kv) * D]).  Returns a dict of fp64 values before rounding
+    (q_val [T,H_q,D], k_val, v_val [T,H_kv,D]), fp8 scales (q_scale [T,H_q],
+    k_scale, v_scale [T,H_kv]) and codes (q_code, k_code, v_code, uint8)."""
+    qkv = _c(qkv, np.uint16)
+    T = qkv.shape[0]
+    Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
+    if qkv.size != T * (Hq + 2 * Hkv) * D:
+        raise ValueError("qkv must be [T, (H_q + 2 H_kv) * D]")
+    pos = _c(positions, np.int32)
+    qw = _c(q_norm_w, np.float32)
+    kw = _c(k_norm_w, np.float32)
+    out = {
+        "q_val": np.zeros((T, Hq, D)), "k_val": np.zeros((T, Hkv, D)),
+        "v_val": np.zeros((T, Hkv, D)), "q_scale": np.zeros((T, Hq)),
+        "k_scale": np.zeros((T, Hkv)), "v_scale": np.zeros((T, Hkv)),
+        "q_code": np.zeros((T, Hq, D), np.uint8), "k_code": np.zeros((T, Hkv, D), np.uint8),
+        "v_code": np.zeros((T, Hkv, D), np.uint8)}
+    rc = _load().orc_prologue(T, Hq, Hkv, D, _ptr(qkv), _ptr(pos), _ptr(qw), _ptr(kw),
+                              float(eps), 1 if rope else 0, float(rope_base),
+                              1 if hadamard else 0,
+                              *[_ptr(out[k]) for k in ("q_val", "k_val", "v_val", "q_scale",
+                                                        "k_scale", "v_scale", "q_code",
+                                                        "k_code", "v_code")])
+    if rc:
+        raise RuntimeError("orc_prologue failed")
+    return out

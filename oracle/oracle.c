@@ -473,3 +473,143 @@ void orc_set_threads(int32_t n)
     (void)n;
 #endif
 }
+
+/* ------------------------------------------------------------------ */
+/* The attention prologue after the QKV projection ([HPC-Ops] "Fused  */
+/* attention prologue"; [Hy3] 2.2.1 "Fused Rope+Norm+[Hadamard]+Quant */
+/* +Store KV"): QK-Norm before RoPE, an optional Hadamard rotation of  */
+/* Q and K before quantisation ([Hy3] 2.6.1, online rotation), Q      */
+/* quantised to fp8 with a per-token per-head scale, K and V quantised */
+/* and written straight into the paged cache.                          */
+/*                                                                      */
+/* Readings where the pages are silent:                                 */
+/*  - QK-Norm is RMSNorm over each head's D values with a learned       */
+/*    weight per dimension (one for Q, one for K):                      */
+/*      y_i = x_i * w_i / sqrt(mean_j x_j^2 + eps);                      */
+/*  - RoPE rotates the pairs (i, i + D/2), i < D/2, by pos * theta_i,   */
+/*    theta_i = base^(-2i/D): y_i = x_i c - x_{i+D/2} s,                */
+/*    y_{i+D/2} = x_{i+D/2} c + x_i s;                                   */
+/*  - the Hadamard rotation is y = H_D x / sqrt(D) with the Sylvester   */
+/*    matrix H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]];               */
+/*  - V is only quantised and stored;                                    */
+/*  - a row's scale is amax / 448 (1 for an all-zero row) and its codes */
+/*    are x / scale rounded to the nearest E4M3FN value, ties to the    */
+/*    even code, saturating at +-448.                                    */
+/* ------------------------------------------------------------------ */
+
+/* Nearest E4M3FN code to v (ties to the code with an even mantissa,   */
+/* |v| > 448 saturates), by comparing against every finite code.       */
+int32_t orc_e4m3_encode(double v)
+{
+    int neg = v < 0 || (v == 0 && signbit(v));
+    double a = fabs(v);
+    if (a > 448.0)
+        a = 448.0;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c < 0x7F; ++c) { /* 0x00 .. 0x7E: the finite non-negative codes */
+        double err = fabs(orc_e4m3_value(c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best_err = err;
+            best = c;
+        }
+    }
+    return neg ? (best | 0x80) : best;
+}
+
+/* Entry (i, j) of the Sylvester Hadamard matrix: (-1)^popcount(i & j). */
+static int sylvester(int i, int j)
+{
+    return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
+}
+
+/* One head vector of D values: RMSNorm (if w), RoPE (if rope), Hadamard
+ * (if hadamard), in that order.  In place. */
+static void prologue_vector(double *x, int D, const float *w, double eps, int rope, double pos,
+                            double base, int hadamard, double *tmp)
+{
+    if (w) {
+        double ss = 0.0;
+        for (int i = 0; i < D; ++i)
+            ss += x[i] * x[i];
+        double inv = 1.0 / sqrt(ss / D + eps);
+        for (int i = 0; i < D; ++i)
+            x[i] = x[i] * inv * (double)w[i];
+    }
+    if (rope) {
+        int half = D / 2;
+        for (int i = 0; i < half; ++i) {
+            double theta = pos * pow(base, -2.0 * i / D);
+            double c = cos(theta), s = sin(theta);
+            double a = x[i], b = x[i + half];
+            x[i] = a * c - b * s;
+            x[i + half] = b * c + a * s;
+        }
+    }
+    if (hadamard) {
+        for (int i = 0; i < D; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < D; ++j)
+                acc += sylvester(i, j) * x[j];
+            tmp[i] = acc / sqrt((double)D);
+        }
+        memcpy(x, tmp, sizeof(double) * D);
+    }
+}
+
+/* The prologue for T tokens.
+ *   qkv       [T, (H_q + 2 H_kv) * D] bf16 bits: Q heads, then K, then V
+ *   positions [T] int32, cache_slots [T] int32 (page * 64 + slot, or < 0:
+ *             not stored)
+ *   q_norm_w, k_norm_w [D] fp32 (NULL: no QK-Norm)
+ * Outputs (fp64, before any rounding to the cache format):
+ *   q_val [T, H_q, D], k_val [T, H_kv, D], v_val [T, H_kv, D]
+ * and, for the fp8 format, per-row scales and codes:
+ *   q_scale [T, H_q], k_scale / v_scale [T, H_kv], q_code [T, H_q, D],
+ *   k_code / v_code [T, H_kv, D]  (any of these may be NULL). */
+int orc_prologue(int32_t T, int32_t H_q, int32_t H_kv, int32_t D, const uint16_t *qkv,
+                 const int32_t *positions, const float *q_norm_w, const float *k_norm_w,
+                 double eps, int32_t rope, double rope_base, int32_t hadamard,
+                 double *q_val, double *k_val, double *v_val,
+                 double *q_scale, double *k_scale, double *v_scale,
+                 uint8_t *q_code, uint8_t *k_code, uint8_t *v_code)
+{
+    const int heads = H_q + 2 * H_kv;
+    int err = 0;
+#pragma omp parallel for schedule(static) reduction(| : err)
+    for (int64_t th = 0; th < (int64_t)T * heads; ++th) {
+        int t = (int)(th / heads), j = (int)(th % heads);
+        double *x = (double *)malloc(sizeof(double) * D * 2);
+        if (!x) {
+            err |= 1;
+            continue;
+        }
+        double *tmp = x + D;
+        const uint16_t *src = qkv + ((int64_t)t * heads + j) * D;
+        for (int i = 0; i < D; ++i)
+            x[i] = orc_bf16_value(src[i]);
+        int kind = j < H_q ? 0 : (j < H_q + H_kv ? 1 : 2);
+        int hh = kind == 0 ? j : (kind == 1 ? j - H_q : j - H_q - H_kv);
+        if (kind < 2)
+            prologue_vector(x, D, kind == 0 ? q_norm_w : k_norm_w, eps, rope, positions[t],
+                            rope_base, hadamard, tmp);
+        double *val = kind == 0 ? q_val : (kind == 1 ? k_val : v_val);
+        double *scl = kind == 0 ? q_scale : (kind == 1 ? k_scale : v_scale);
+        uint8_t *code = kind == 0 ? q_code : (kind == 1 ? k_code : v_code);
+        int64_t row = (int64_t)t * (kind == 0 ? H_q : H_kv) + hh;
+        if (val)
+            memcpy(val + row * D, x, sizeof(double) * D);
+        double amax = 0.0;
+        for (int i = 0; i < D; ++i)
+            if (fabs(x[i]) > amax)
+                amax = fabs(x[i]);
+        double scale = amax > 0 ? amax / 448.0 : 1.0;
+        if (scl)
+            scl[row] = scale;
+        if (code)
+            for (int i = 0; i < D; ++i)
+                code[row * D + i] = (uint8_t)orc_e4m3_encode(x[i] / scale);
+        free(x);
+    }
+    return err ? -1 : 0;
+}
