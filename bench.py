@@ -54,7 +54,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixed", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--workload", default="mixed", choices=sorted(DESCRIPTIONS) + ["prologue"])
     ap.add_argument("--num-bins", type=int, default=None)
     ap.add_argument("--min-tiles", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None,
@@ -127,6 +127,145 @@ def calibrate():
         "chunked_16k_read_best_GBs": max(chunked.values())}), flush=True)
 
 
+def prologue_bench(reps=20):
+    """The fused prologue (QK-Norm, RoPE, Hadamard, quantisation, KV store)
+    at a decode shape (64 tokens, one per request) and a prefill shape
+    (16384 tokens), 64 Q / 8 KV heads, D = 128, bf16 in; fp8 and bf16 out.
+    Bytes = bf16 QKV read + norm weights + positions / slots + Q, K, V (and
+    scales) written; timed as a HIP graph of `reps` launches."""
+    import numpy as np
+    import torch
+
+    from load_balanced_split_amd import hpcattn as H
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    Hq, Hkv, D = 64, 8, 128
+    res = {}
+    for T in (64, 16384):
+        for fp8 in (True, False):
+            num_pages = (T + 63) // 64 + 1
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(T)
+            qkv = torch.randn((T, (Hq + 2 * Hkv) * D), generator=gen, device="cuda").to(
+                torch.bfloat16)
+            pos = torch.arange(T, dtype=torch.int32, device="cuda")
+            slots = torch.randperm(num_pages * 64, generator=torch.Generator().manual_seed(T))[
+                :T].to(torch.int32).cuda()
+            w = torch.ones(D, device="cuda")
+            dt = torch.uint8 if fp8 else torch.bfloat16
+            q_out = torch.empty((T, Hq, D), dtype=dt, device="cuda")
+            kp = torch.zeros((num_pages, Hkv, 64, D), dtype=dt, device="cuda")
+            vp = torch.zeros_like(kp)
+            sc = {}
+            if fp8:
+                sc = dict(q_scale=torch.empty((T, Hq), device="cuda"),
+                          k_scale=torch.zeros((num_pages, Hkv, 64), device="cuda"),
+                          v_scale=torch.zeros((num_pages, Hkv, 64), device="cuda"))
+            dims = H.hpcattn_prologue_dims(T, Hq, Hkv, D, num_pages,
+                                           H.KV_FP8_E4M3 if fp8 else H.KV_BF16,
+                                           H.PROLOGUE_ROPE | H.PROLOGUE_HADAMARD, 1e-6, 10000.0)
+
+            def call():
+                H.hpcattn_prologue(dims, qkv, pos, slots, q_out, kp, vp, q_norm_w=w,
+                                   k_norm_w=w, **sc)
+            call()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    call()
+            g.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            b.synchronize()
+            us = a.elapsed_time(b) / reps * 1e3
+            unfused_us = unfused_prologue_us(qkv, pos, slots, w, kp, vp, sc, Hq, Hkv, D, fp8,
+                                             stream, reps)
+            esz = 1 if fp8 else 2
+            nbytes = (T * (Hq + 2 * Hkv) * D * 2 + 2 * D * 4 + 2 * T * 4
+                      + T * (Hq + 2 * Hkv) * D * esz + (T * (Hq + 2 * Hkv) * 4 if fp8 else 0))
+            res["T=%d %s" % (T, "fp8" if fp8 else "bf16")] = {
+                "us": round(us, 2), "unfused_torch_us": round(unfused_us, 2),
+                "speedup_vs_unfused": round(unfused_us / us, 2), "bytes": nbytes,
+                "GBs": round(nbytes / us / 1e3, 1),
+                "pct_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1)}
+    print(json.dumps({"prologue": "QK-Norm + RoPE + Hadamard + quantise + KV store, "
+                                  "64 Q / 8 KV heads, D 128, bf16 in", "results": res}),
+          flush=True)
+
+
+def unfused_prologue_us(qkv, pos, slots, w, kp, vp, sc, Hq, Hkv, D, fp8, stream, reps):
+    """The same prologue as separate PyTorch GPU operations (each step a kernel
+    with its own HBM round trip), the unfused chain the fused kernel replaces:
+    RMSNorm, RoPE from precomputed cos/sin tables, Hadamard as a matmul,
+    per-row quantisation, KV scatter.  Timed the same way (HIP graph)."""
+    import math
+
+    import scipy.linalg
+    import torch
+    T = qkv.shape[0]
+    half = D // 2
+    inv = 10000.0 ** (-2.0 * torch.arange(half, dtype=torch.float64, device="cuda") / D)
+    ang = pos.double()[:, None] * inv[None, :]
+    cos, sin = ang.cos().float(), ang.sin().float()
+    Hd = torch.from_numpy(scipy.linalg.hadamard(D) / math.sqrt(D)).float().cuda()
+    q_out = torch.empty((T, Hq, D), dtype=torch.uint8 if fp8 else torch.bfloat16,
+                        device="cuda")
+    kflat = kp.view(-1, Hkv, D)
+    vflat = vp.view(-1, Hkv, D)
+    sl = slots.long()
+
+    def step():
+        x = qkv.view(T, Hq + 2 * Hkv, D).float()
+        q, k, v = x[:, :Hq], x[:, Hq:Hq + Hkv], x[:, Hq + Hkv:]
+        q = q * torch.rsqrt(q.pow(2).mean(-1, keepdim=True) + 1e-6) * w
+        k = k * torch.rsqrt(k.pow(2).mean(-1, keepdim=True) + 1e-6) * w
+        c, s_ = cos[:, None, :], sin[:, None, :]
+        q = torch.cat([q[..., :half] * c - q[..., half:] * s_,
+                       q[..., half:] * c + q[..., :half] * s_], -1)
+        k = torch.cat([k[..., :half] * c - k[..., half:] * s_,
+                       k[..., half:] * c + k[..., :half] * s_], -1)
+        q = q @ Hd.T
+        k = k @ Hd.T
+        if fp8:
+            outs = []
+            for t_ in (q, k, v):
+                amax = t_.abs().amax(-1, keepdim=True)
+                scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+                outs.append(((t_ / scale).clamp(-448, 448).to(torch.float8_e4m3fn)
+                             .view(torch.uint8), scale.squeeze(-1)))
+            q_out.copy_(outs[0][0])
+            sc["q_scale"].copy_(outs[0][1])
+            kflat[sl] = outs[1][0]
+            vflat[sl] = outs[2][0]
+            sc["k_scale"].view(-1, Hkv)[sl] = outs[1][1]
+            sc["v_scale"].view(-1, Hkv)[sl] = outs[2][1]
+        else:
+            q_out.copy_(q.to(torch.bfloat16))
+            kflat[sl] = k.to(torch.bfloat16)
+            vflat[sl] = v.to(torch.bfloat16)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps * 1e3
+
+
 def traffic_from_profile():
     """HBM bytes per decode launch from the committed counter summary, if it
     was taken on the current decode source."""
@@ -186,6 +325,9 @@ def main():
     args = parse_args()
     if args.calibrate:
         calibrate()
+        return
+    if args.workload == "prologue":
+        prologue_bench()
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

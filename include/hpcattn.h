@@ -237,6 +237,55 @@ int64_t hpcattn_static_max_partials(int32_t batch, int32_t num_kv_heads, int32_t
 int hpcattn_probe_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
                               uint32_t *sink, void *stream);
 
+/* Prologue flags. */
+#define HPCATTN_PROLOGUE_ROPE 1      /* rotate Q and K by their positions      */
+#define HPCATTN_PROLOGUE_HADAMARD 2  /* rotate Q and K by H_D / sqrt(D)         */
+
+/* Shape and options of one prologue call (host struct). */
+typedef struct {
+    int32_t num_tokens;         /* T >= 0 tokens (one per request in decode)  */
+    int32_t num_q_heads;        /* H_q >= 1                                   */
+    int32_t num_kv_heads;       /* H_kv >= 1                                  */
+    int32_t head_dim;           /* D, 64 or 128                               */
+    int32_t num_pages;          /* pages in k_pages / v_pages                 */
+    int32_t kv_dtype;           /* HPCATTN_KV_BF16 or HPCATTN_KV_FP8_E4M3     */
+    int32_t flags;              /* HPCATTN_PROLOGUE_* bits                    */
+    float eps;                  /* RMSNorm epsilon, >= 0                      */
+    float rope_base;            /* RoPE base (e.g. 10000), > 0                */
+} hpcattn_prologue_dims;
+
+/*
+ * The attention prologue, fused ("Fused attention prologue": QK-Norm before
+ * RoPE, Q in FP8 with per-token per-head scales passed to attention as is,
+ * K and V written straight into the paged FP8 cache; "Hy3 preview full-stack
+ * inference optimization" 2.2.1: RoPE + RMSNorm + optional Hadamard +
+ * quantisation + KV store in one kernel).  For each token t and head:
+ *   Q, K:  x <- x * w / sqrt(mean(x^2) + eps)        (if q_norm_w / k_norm_w)
+ *          (x_i, x_{i+D/2}) rotated by positions[t] * base^(-2i/D)  (ROPE)
+ *          x <- H_D x / sqrt(D), Sylvester H_D                       (HADAMARD)
+ *   V:     unchanged.
+ * Outputs, bf16 format: q_out [T, H_q, D] bf16; K, V rows into the bf16
+ * cache.  fp8 format: each row (one token, one head) gets scale
+ * amax / 448 (1 if all zero) and codes RNE(x / scale) in OCP E4M3FN:
+ * q_out [T, H_q, D] bytes + q_scale [T, H_q]; K, V rows + k_scale, v_scale
+ * entries in the paged cache and its scale pools.
+ *
+ * qkv          device bf16 [T, (H_q + 2 H_kv) * D]: Q heads, then K, then V
+ * positions    device int32 [T] (needed with ROPE, else may be NULL)
+ * cache_slots  device int32 [T]: page * 64 + slot of token t's K/V in the
+ *              cache; a negative slot (or a page >= num_pages) stores nothing
+ * q_norm_w, k_norm_w  device fp32 [D] or NULL (no QK-Norm)
+ * q_scale, k_scale, v_scale: required for fp8, NULL for bf16.
+ * Writes only q_out/q_scale rows of the T tokens and the cache rows named by
+ * cache_slots.  Errors: NULL pointers, sizes out of range, unknown flags or
+ * dtype, eps < 0, rope_base <= 0.
+ */
+int hpcattn_prologue(const hpcattn_prologue_dims *dims, const void *qkv,
+                     const int32_t *positions, const int32_t *cache_slots,
+                     const float *q_norm_w, const float *k_norm_w, void *q_out, float *q_scale,
+                     void *k_pages, void *v_pages, float *k_scale, float *v_scale,
+                     void *stream);
+
 /* Static description of a status code (host string, never NULL). */
 const char *hpcattn_strerror(int status);
 

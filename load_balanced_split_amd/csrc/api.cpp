@@ -234,6 +234,49 @@ int hpcattn_probe_stream_read(const void *buf, size_t bytes, int32_t workgroups,
         launch_stream_read(buf, bytes, workgroups, flags, sink, (hipStream_t)stream));
 }
 
+int hpcattn_prologue(const hpcattn_prologue_dims *d, const void *qkv, const int32_t *positions,
+                     const int32_t *cache_slots, const float *q_norm_w, const float *k_norm_w,
+                     void *q_out, float *q_scale, void *k_pages, void *v_pages, float *k_scale,
+                     float *v_scale, void *stream) {
+    if (!d) return HPCATTN_ERR_NULL;
+    if (d->num_tokens < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
+        (d->head_dim != 64 && d->head_dim != 128) || d->num_pages < 1 ||
+        (int64_t)d->num_tokens * (d->num_q_heads + 2 * d->num_kv_heads) > INT32_MAX * 4ll)
+        return HPCATTN_ERR_SHAPE;
+    if (d->kv_dtype != HPCATTN_KV_BF16 && d->kv_dtype != HPCATTN_KV_FP8_E4M3)
+        return HPCATTN_ERR_DTYPE;
+    if ((d->flags & ~(HPCATTN_PROLOGUE_ROPE | HPCATTN_PROLOGUE_HADAMARD)) ||
+        !(d->eps >= 0.f) || !std::isfinite(d->eps) || !(d->rope_base > 0.f) ||
+        !std::isfinite(d->rope_base))
+        return HPCATTN_ERR_ARG;
+    if (!qkv || !cache_slots || !q_out || !k_pages || !v_pages) return HPCATTN_ERR_NULL;
+    if ((d->flags & HPCATTN_PROLOGUE_ROPE) && !positions) return HPCATTN_ERR_NULL;
+    const bool fp8 = d->kv_dtype == HPCATTN_KV_FP8_E4M3;
+    if (fp8 ? !(q_scale && k_scale && v_scale) : (q_scale || k_scale || v_scale))
+        return HPCATTN_ERR_DTYPE;
+    PrologueParams p{};
+    p.qkv = qkv;
+    p.positions = positions;
+    p.cache_slots = cache_slots;
+    p.q_norm_w = q_norm_w;
+    p.k_norm_w = k_norm_w;
+    p.q_out = q_out;
+    p.q_scale = q_scale;
+    p.k_pages = k_pages;
+    p.v_pages = v_pages;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.T = d->num_tokens;
+    p.Hq = d->num_q_heads;
+    p.Hkv = d->num_kv_heads;
+    p.num_pages = d->num_pages;
+    p.kv_dtype = d->kv_dtype;
+    p.flags = d->flags;
+    p.eps = d->eps;
+    p.log2_base = std::log2((double)d->rope_base);
+    return launch_status(launch_prologue(p, d->head_dim, (hipStream_t)stream));
+}
+
 const char *hpcattn_strerror(int status) {
     switch (status) {
     case HPCATTN_OK: return "ok";

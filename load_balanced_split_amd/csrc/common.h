@@ -58,6 +58,25 @@ struct CombineParams {
     int32_t S, G, D;
 };
 
+// Arguments of the prologue kernel.
+struct PrologueParams {
+    const void *qkv;
+    const int32_t *positions;
+    const int32_t *cache_slots;
+    const float *q_norm_w;
+    const float *k_norm_w;
+    void *q_out;
+    float *q_scale;
+    void *k_pages;
+    void *v_pages;
+    float *k_scale;
+    float *v_scale;
+    int32_t T, Hq, Hkv, num_pages, kv_dtype, flags;
+    int32_t chunks;     // groups of 4 heads per wave (set by the launcher)
+    float eps;
+    double log2_base;   // log2 of the RoPE base
+};
+
 hipError_t launch_plan(const int32_t *seq_lens, int32_t B, int32_t Hkv, int32_t P,
                        int32_t m, int32_t *map, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dtype,
@@ -65,6 +84,7 @@ hipError_t launch_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dty
 hipError_t launch_static_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dtype,
                                 hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+hipError_t launch_prologue(const PrologueParams &p, int32_t head_dim, hipStream_t stream);
 int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t group);
 hipError_t launch_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
                               uint32_t *sink, hipStream_t stream);

@@ -44,6 +44,23 @@ class hpcattn_dims(ctypes.Structure):
     ]
 
 
+PROLOGUE_ROPE, PROLOGUE_HADAMARD = 1, 2
+
+
+class hpcattn_prologue_dims(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("rope_base", ctypes.c_float),
+    ]
+
+
 class hpcattn_task_map(ctypes.Structure):
     _fields_ = [
         ("words", ctypes.c_void_p),
@@ -74,6 +91,8 @@ _sig = {
                                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _i64, _vp, _vp, _vp]),
     "hpcattn_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _vp, _vp]),
+    "hpcattn_prologue": (ctypes.c_int, [ctypes.POINTER(hpcattn_prologue_dims), _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hpcattn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "hpcattn_version": (ctypes.c_int, []),
 }
@@ -220,3 +239,14 @@ def hpcattn_probe_stream_read(buf, workgroups: int, sink, nontemporal: bool = Fa
     _check(_lib.hpcattn_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
                                           workgroups, flags, _ptr(sink), _stream(stream)),
            "hpcattn_probe_stream_read")
+
+
+def hpcattn_prologue(dims: hpcattn_prologue_dims, qkv, positions, cache_slots, q_out,
+                     k_pages, v_pages, q_norm_w=None, k_norm_w=None, q_scale=None,
+                     k_scale=None, v_scale=None, stream=None) -> None:
+    """QK-Norm -> RoPE -> [Hadamard] -> quantise Q and store K/V in the cache."""
+    _check(_lib.hpcattn_prologue(ctypes.byref(dims), _ptr(qkv), _ptr(positions),
+                                 _ptr(cache_slots), _ptr(q_norm_w), _ptr(k_norm_w),
+                                 _ptr(q_out), _ptr(q_scale), _ptr(k_pages), _ptr(v_pages),
+                                 _ptr(k_scale), _ptr(v_scale), _stream(stream)),
+           "hpcattn_prologue")

@@ -148,6 +148,32 @@ def test_suggest_and_probe_reject_bad_arguments(H):
     assert lib.hpcattn_probe_stream_read(FAKE, 3 * 16384, 8, 2, FAKE, None) == H.ERR_ARG
 
 
+def test_prologue_rejects_bad_arguments(H):
+    lib = H._lib
+
+    def pro(fp8=False, scales=False, flags=1, eps=1e-6, base=10000.0, D=128, T=4, nulls=()):
+        d = H.hpcattn_prologue_dims(T, 8, 2, D, 4, H.KV_FP8_E4M3 if fp8 else H.KV_BF16, flags,
+                                    eps, base)
+        ptr = {k: (None if k in nulls else FAKE) for k in
+               ("qkv", "pos", "slots", "q", "k", "v")}
+        sc = FAKE if scales else None
+        return lib.hpcattn_prologue(ctypes.byref(d), ptr["qkv"], ptr["pos"], ptr["slots"],
+                                    None, None, ptr["q"], sc, ptr["k"], ptr["v"], sc, sc, None)
+
+    assert lib.hpcattn_prologue(None, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE,
+                                None, None, None) == H.ERR_NULL
+    assert pro(D=96) == H.ERR_SHAPE
+    assert pro(T=-1) == H.ERR_SHAPE
+    assert pro(flags=4) == H.ERR_ARG
+    assert pro(eps=-1.0) == H.ERR_ARG
+    assert pro(base=0.0) == H.ERR_ARG
+    assert pro(nulls=("qkv",)) == H.ERR_NULL
+    assert pro(nulls=("slots",)) == H.ERR_NULL
+    assert pro(nulls=("pos",)) == H.ERR_NULL             # RoPE needs positions
+    assert pro(fp8=True, scales=False) == H.ERR_DTYPE     # fp8 needs scales
+    assert pro(fp8=False, scales=True) == H.ERR_DTYPE     # bf16 takes none
+
+
 def test_strerror_covers_every_status(H):
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert H.hpcattn_strerror(code) != "unknown status"
