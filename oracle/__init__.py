@@ -11,10 +11,13 @@ citing the passage of the pages it follows ("HPC-Ops x SGLang", sections
 live KV work"; "Hy3 preview full-stack inference optimization", section 2.1.1).
 
 Arrays:
-  q          [B, H_q, D]              uint16 (bf16 bits) or uint8 (e4m3 bytes)
+  q          [B, H_q, D]              uint16 (bf16 bits) or uint8 (e4m3 bytes),
+             or [B, R, H_q, D] for R query rows per request (the confirmed
+             token and R - 1 drafts: row r sits at position L_b - R + r and
+             sees tokens [0, L_b - R + r]); outputs then carry the R axis too
   k_pages    [num_pages, H_kv, 64, D] same element type as q
   v_pages    [num_pages, H_kv, 64, D]
-  q_scale    [B, H_q] float32          fp8 only
+  q_scale    [B, H_q] (or [B, R, H_q]) float32, fp8 only
   k_scale    [num_pages, H_kv, 64] float32, v_scale likewise (fp8 only)
   page_table [B, max_pages] int32
   seq_lens   [B] int32
@@ -60,7 +63,7 @@ class _Dims(ctypes.Structure):
         ("max_pages", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
         ("kv_fp8", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("q_rows", ctypes.c_int32),
         ("sm_scale", ctypes.c_double),
     ]
 
@@ -78,7 +81,8 @@ def _load():
             lib.orc_bf16_value.restype = f64
             lib.orc_e4m3_value.argtypes = [i32]
             lib.orc_e4m3_value.restype = f64
-            lib.orc_attend_range.argtypes = [dp, P, P, P, P, P, P, P, i32, i32, i32, i32, P, P]
+            lib.orc_attend_range.argtypes = [dp, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                             P, P]
             lib.orc_attend_range.restype = ctypes.c_int
             lib.orc_attention.argtypes = [dp, P, P, P, P, P, P, P, P, P, i32, P, P]
             lib.orc_attention.restype = ctypes.c_int
@@ -126,7 +130,15 @@ class _Inputs:
         self.k = _c(k_pages, et)
         self.v = _c(v_pages, et)
         self.pt = _c(page_table, np.int32)
-        B, Hq, D = self.q.shape
+        if self.q.ndim == 3:
+            B, Hq, D = self.q.shape
+            self.R = 1
+        elif self.q.ndim == 4:
+            B, self.R, Hq, D = self.q.shape
+        else:
+            raise ValueError("q must be [B, H_q, D] or [B, R, H_q, D]")
+        if self.R < 1:
+            raise ValueError("at least one query row per request")
         if self.k.shape[1:] != (num_kv_heads, TILE, D) or self.v.shape != self.k.shape:
             raise ValueError("k/v pools must be [num_pages, H_kv, 64, D]")
         if Hq % num_kv_heads:
@@ -140,7 +152,8 @@ class _Inputs:
         else:
             self.qs = self.ks = self.vs = None
         self.dims = _Dims(B, Hq, num_kv_heads, D, self.pt.shape[1], self.k.shape[0],
-                          1 if fp8 else 0, 0, float(sm_scale))
+                          1 if fp8 else 0, self.R, float(sm_scale))
+        self.B, self.Hq, self.D = B, Hq, D
         self.G = Hq // num_kv_heads
 
     def args(self):
@@ -162,14 +175,18 @@ def e4m3_table() -> np.ndarray:
 
 
 def attend_range(q, k_pages, v_pages, page_table, b, h, tok0, tok1, *, num_kv_heads,
-                 sm_scale, q_scale=None, k_scale=None, v_scale=None):
-    """Attention of the G query heads of (request b, KV head h) over tokens
-    [tok0, tok1).  Returns (o [G, D], lse [G]) in fp64."""
+                 sm_scale, q_scale=None, k_scale=None, v_scale=None, seq_len=None):
+    """Attention of the query rows of (request b, KV head h) over tokens
+    [tok0, tok1), row r within its visible length seq_len - (R - 1 - r)
+    (seq_len defaults to tok1).  Returns (o [R G, D], lse [R G]) in fp64,
+    row r G + g for query head h G + g."""
     x = _Inputs(q, k_pages, v_pages, page_table, num_kv_heads, sm_scale,
                 q_scale, k_scale, v_scale)
-    o = np.zeros((x.G, x.dims.head_dim), np.float64)
-    lse = np.zeros((x.G,), np.float64)
-    rc = _load().orc_attend_range(*x.args(), int(b), int(h), int(tok0), int(tok1),
+    n = x.R * x.G
+    o = np.zeros((n, x.D), np.float64)
+    lse = np.zeros((n,), np.float64)
+    ln = tok1 if seq_len is None else seq_len
+    rc = _load().orc_attend_range(*x.args(), int(b), int(h), int(tok0), int(tok1), int(ln),
                                   _ptr(o), _ptr(lse))
     if rc:
         raise RuntimeError("orc_attend_range failed")
@@ -181,13 +198,14 @@ def attention(q, k_pages, v_pages, page_table, seq_lens, *, num_kv_heads, sm_sca
     """Decode attention of every request over its whole live KV.
 
     pairs: optional iterable of (b, h) to compute; other rows stay NaN.
-    Returns (out [B, H_q, D], lse [B, H_q]) in fp64."""
+    Returns (out, lse) in fp64, shaped like q without D: [B, H_q, D] and
+    [B, H_q], or [B, R, H_q, D] and [B, R, H_q]."""
     x = _Inputs(q, k_pages, v_pages, page_table, num_kv_heads, sm_scale,
                 q_scale, k_scale, v_scale)
     lens = _c(seq_lens, np.int32)
-    B, Hq, D = x.q.shape
-    out = np.full((B, Hq, D), np.nan, np.float64)
-    lse = np.full((B, Hq), np.nan, np.float64)
+    lead = x.q.shape[:-1]
+    out = np.full(lead + (x.D,), np.nan, np.float64)
+    lse = np.full(lead, np.nan, np.float64)
     pr = None if pairs is None else np.ascontiguousarray(np.asarray(pairs, np.int32).reshape(-1, 2))
     n = 0 if pr is None else pr.shape[0]
     rc = _load().orc_attention(*x.args(), _ptr(lens), _ptr(pr), n, _ptr(out), _ptr(lse))
@@ -239,31 +257,34 @@ def parse_map(words, num_bins: int) -> dict:
 
 def partials(q, k_pages, v_pages, page_table, task_map, num_bins, *, num_kv_heads,
              sm_scale, q_scale=None, k_scale=None, v_scale=None):
-    """Per-descriptor partial (o, lse) following a task map."""
+    """Per-descriptor partial (o [num_desc, R G, D], lse [num_desc, R G])
+    following a task map."""
     x = _Inputs(q, k_pages, v_pages, page_table, num_kv_heads, sm_scale,
                 q_scale, k_scale, v_scale)
     m = _c(task_map, np.int32)
     nd = int(m[4])
-    po = np.zeros((max(nd, 1), x.G, x.dims.head_dim), np.float64)
-    pl = np.zeros((max(nd, 1), x.G), np.float64)
+    po = np.zeros((max(nd, 1), x.R * x.G, x.D), np.float64)
+    pl = np.zeros((max(nd, 1), x.R * x.G), np.float64)
     rc = _load().orc_partials(*x.args(), _ptr(m), int(num_bins), _ptr(po), _ptr(pl))
     if rc:
         raise RuntimeError("orc_partials failed")
     return po[:nd], pl[:nd]
 
 
-def combine(task_map, num_bins, part_o, part_lse, *, num_q_heads, head_dim):
-    """Merge per-descriptor partials into (out [B, H_q, D], lse [B, H_q])."""
+def combine(task_map, num_bins, part_o, part_lse, *, num_q_heads, head_dim, q_rows=1):
+    """Merge per-descriptor partials into (out [B, H_q, D], lse [B, H_q]),
+    or [B, R, H_q, D] and [B, R, H_q] for q_rows = R > 1."""
     m = _c(task_map, np.int32)
     B, Hkv = int(m[5]), int(m[6])
-    dims = _Dims(B, num_q_heads, Hkv, head_dim, 0, 0, 0, 0, 0.0)
+    dims = _Dims(B, num_q_heads, Hkv, head_dim, 0, 0, 0, int(q_rows), 0.0)
     po = _c(part_o, np.float64)
     pl = _c(part_lse, np.float64)
     if po.size == 0:
         po = np.zeros((1,), np.float64)
         pl = np.zeros((1,), np.float64)
-    out = np.zeros((B, num_q_heads, head_dim), np.float64)
-    lse = np.zeros((B, num_q_heads), np.float64)
+    lead = (B, num_q_heads) if q_rows == 1 else (B, int(q_rows), num_q_heads)
+    out = np.zeros(lead + (head_dim,), np.float64)
+    lse = np.zeros(lead, np.float64)
     rc = _load().orc_combine(ctypes.byref(dims), _ptr(m), int(num_bins), _ptr(po), _ptr(pl),
                              _ptr(out), _ptr(lse))
     if rc:

@@ -14,7 +14,11 @@
  *             "Attention: load balancing for variable-length decode" and
  *             "Scheduling around live KV work", and "Fused attention prologue".
  *   [Hy3]     "Hy3 preview full-stack inference optimization", section 2.1.1
- *             "Attention dynamic scheduling".
+ *             "Attention dynamic scheduling", and section 2.5 (MTP: the
+ *             target model verifies the draft tokens of a step).
+ *   [LowLat]  "SGLang Low-Latency Mode: Kernels and Runtime", section 1: a
+ *             verify step runs one forward over six rows per request, the
+ *             confirmed token and five drafts.
  *
  * Parity pins (all in the CPU test suite): a numpy brute-force softmax on tiny
  * inputs, torch float64 scaled-dot-product attention as a library routine,
@@ -44,7 +48,7 @@ typedef struct {
     int32_t max_pages;    /* columns of page_table                       */
     int32_t num_pages;    /* pages in each KV pool                       */
     int32_t kv_fp8;       /* 0: bf16 q/k/v; 1: fp8 e4m3 bytes + scales   */
-    int32_t reserved;     /* keeps sm_scale 8-byte aligned               */
+    int32_t q_rows;       /* R >= 1 query rows per request (1 + drafts)  */
     double sm_scale;      /* softmax scale applied to q.k                */
 } orc_dims;
 
@@ -82,10 +86,17 @@ double orc_e4m3_value(int32_t code)
     return sign ? -mag : mag;
 }
 
+/* Query rows per request: R = 1 for plain decode, 1 + k when a step     */
+/* verifies k draft tokens in one forward ([Hy3] 2.5; [LowLat] 1).      */
+static int rows_of(const orc_dims *dm)
+{
+    return dm->q_rows > 1 ? dm->q_rows : 1;
+}
+
 /* ------------------------------------------------------------------ */
 /* Paged KV access.                                                     */
-/*   q          [B, H_q, D]            bf16 bits or e4m3 bytes         */
-/*   q_scale    [B, H_q]               fp32 (fp8 only)                 */
+/*   q          [B, R, H_q, D]         bf16 bits or e4m3 bytes         */
+/*   q_scale    [B, R, H_q]            fp32 (fp8 only)                 */
 /*   k/v pools  [num_pages, H_kv, 64, D]                               */
 /*   k/v scale  [num_pages, H_kv, 64]  fp32 (fp8 only)                 */
 /*   page_table [B, max_pages]         int32; token t of request b is  */
@@ -93,9 +104,9 @@ double orc_e4m3_value(int32_t code)
 /* ------------------------------------------------------------------ */
 
 static double load_q(const orc_dims *dm, const void *q, const float *q_scale,
-                     int b, int j, int d)
+                     int b, int r, int j, int d)
 {
-    int64_t row = (int64_t)b * dm->num_q_heads + j;
+    int64_t row = ((int64_t)b * rows_of(dm) + r) * dm->num_q_heads + j;
     int64_t idx = row * dm->head_dim + d;
     if (dm->kv_fp8)
         return orc_e4m3_value(((const uint8_t *)q)[idx]) * (double)q_scale[row];
@@ -113,43 +124,58 @@ static double load_kv(const orc_dims *dm, const void *pool, const float *scale,
 }
 
 /* ------------------------------------------------------------------ */
-/* Attention of one decode query row over a token range.               */
+/* Attention of the query rows of one (request, KV head) over a token   */
+/* range.                                                               */
 /*                                                                      */
-/* For request b and query head j (KV head h = j / G, G = H_q / H_kv):  */
+/* For request b, query row r and query head j (KV head h = j / G,      */
+/* G = H_q / H_kv):                                                     */
 /*   s_t = sm_scale * sum_d q_d k_{t,d}                                 */
 /*   M   = max_t s_t,  l = sum_t exp(s_t - M)                           */
 /*   o   = sum_t exp(s_t - M) v_t / l,   lse = M + ln l                 */
-/* over tokens t in [tok0, tok1).  Each new token attends over the      */
-/* whole cached KV of its request, with no other mask ([HPC-Ops]        */
-/* "Attention: load balancing for variable-length decode").  An empty   */
-/* range gives o = 0, lse = -inf.  Computes all G heads of KV head h.   */
+/* over tokens t in [tok0, min(tok1, len - (R - 1 - r))), len = L_b.    */
+/* With R = 1 the new token attends over the whole cached KV of its     */
+/* request, with no other mask ([HPC-Ops] "Attention: load balancing    */
+/* for variable-length decode").  With R > 1 the R rows are the last R  */
+/* tokens of the request (the cache already holds all of them), row r   */
+/* at position len - R + r, and each sees the tokens up to and          */
+/* including its own: a causal mask among the drafts ([Hy3] 2.5 and     */
+/* [LowLat] 1 verify drafts in one forward; the pages give no mask, and */
+/* the causal one is the plain reading of verifying a token sequence).  */
+/* An empty range gives o = 0, lse = -inf.                              */
+/* Writes o [R * G, D] and lse [R * G], row r * G + g for head h G + g. */
 /* ------------------------------------------------------------------ */
 int orc_attend_range(const orc_dims *dm, const void *q, const float *q_scale,
                      const void *k_pages, const void *v_pages,
                      const float *k_scale, const float *v_scale,
                      const int32_t *page_table, int32_t b, int32_t h,
-                     int32_t tok0, int32_t tok1,
-                     double *o /* [G, D] */, double *lse /* [G] */)
+                     int32_t tok0, int32_t tok1, int32_t len,
+                     double *o /* [R * G, D] */, double *lse /* [R * G] */)
 {
     const int D = dm->head_dim;
     const int G = dm->num_q_heads / dm->num_kv_heads;
-    const int n = tok1 > tok0 ? tok1 - tok0 : 0;
-    double *s = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
+    const int R = rows_of(dm);
+    const int span = tok1 > tok0 ? tok1 - tok0 : 0;
+    double *s = (double *)malloc(sizeof(double) * (span > 0 ? span : 1));
     double *qv = (double *)malloc(sizeof(double) * D);
     if (!s || !qv) {
         free(s);
         free(qv);
         return -1;
     }
-    for (int g = 0; g < G; ++g) {
+    for (int c = 0; c < R * G; ++c) {
+        int r = c / G, g = c % G;
         int j = h * G + g;
-        double *og = o + (int64_t)g * D;
+        int end = len - (R - 1 - r);   /* tokens row r may see */
+        if (end > tok1)
+            end = tok1;
+        const int n = end > tok0 ? end - tok0 : 0;
+        double *og = o + (int64_t)c * D;
         for (int d = 0; d < D; ++d) {
-            qv[d] = load_q(dm, q, q_scale, b, j, d);
+            qv[d] = load_q(dm, q, q_scale, b, r, j, d);
             og[d] = 0.0;
         }
         if (n == 0) {
-            lse[g] = -INFINITY;
+            lse[c] = -INFINITY;
             continue;
         }
         double M = -INFINITY;
@@ -174,7 +200,7 @@ int orc_attend_range(const orc_dims *dm, const void *q, const float *q_scale,
         }
         for (int d = 0; d < D; ++d)
             og[d] /= l;
-        lse[g] = M + log(l);
+        lse[c] = M + log(l);
     }
     free(s);
     free(qv);
@@ -183,8 +209,9 @@ int orc_attend_range(const orc_dims *dm, const void *q, const float *q_scale,
 
 /* Full decode attention: every request over its whole live KV.
  * pairs: NULL for all (b, h) pairs, else n_pairs (b, h) int32 pairs; only
- * those rows of out/out_lse are written.  out [B, H_q, D], out_lse [B, H_q].
- * One OpenMP task per (request, KV head), all G query heads together. */
+ * those rows of out/out_lse are written.  out [B, R, H_q, D],
+ * out_lse [B, R, H_q].  One OpenMP task per (request, KV head), all R G
+ * query rows together. */
 int orc_attention(const orc_dims *dm, const void *q, const float *q_scale,
                   const void *k_pages, const void *v_pages,
                   const float *k_scale, const float *v_scale,
@@ -195,16 +222,30 @@ int orc_attention(const orc_dims *dm, const void *q, const float *q_scale,
     const int H_kv = dm->num_kv_heads;
     const int G = dm->num_q_heads / H_kv;
     const int D = dm->head_dim;
+    const int R = rows_of(dm);
     const int64_t total = pairs ? n_pairs : (int64_t)dm->batch * H_kv;
     int err = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int64_t i = 0; i < total; ++i) {
         int b = pairs ? pairs[2 * i] : (int)(i / H_kv);
         int h = pairs ? pairs[2 * i + 1] : (int)(i % H_kv);
-        int64_t row = (int64_t)b * dm->num_q_heads + (int64_t)h * G;
+        double *o = (double *)malloc(sizeof(double) * (size_t)R * G * D);
+        double *l = (double *)malloc(sizeof(double) * (size_t)R * G);
+        if (!o || !l) {
+            free(o);
+            free(l);
+            err |= 1;
+            continue;
+        }
         err |= orc_attend_range(dm, q, q_scale, k_pages, v_pages, k_scale, v_scale,
-                                page_table, b, h, 0, seq_lens[b],
-                                out + row * D, out_lse + row);
+                                page_table, b, h, 0, seq_lens[b], seq_lens[b], o, l);
+        for (int c = 0; c < R * G; ++c) {
+            int64_t row = ((int64_t)b * R + c / G) * dm->num_q_heads + (int64_t)h * G + c % G;
+            memcpy(out + row * D, o + (int64_t)c * D, sizeof(double) * D);
+            out_lse[row] = l[c];
+        }
+        free(o);
+        free(l);
     }
     return err ? -1 : 0;
 }
@@ -380,8 +421,9 @@ int64_t orc_plan(const int32_t *seq_lens, int32_t B, int32_t H_kv, int32_t P,
 }
 
 /* Per-descriptor partials following a task map: descriptor k covers
- * tokens [64 t0, min(64 t1, L_b)) of segment (b, h).  Writes
- * part_o [num_desc, G, D] and part_lse [num_desc, G].  P is the bin count
+ * tokens [64 t0, 64 t1) of segment (b, h), each query row within its own
+ * visible length (orc_attend_range).  Writes part_o [num_desc, R G, D] and
+ * part_lse [num_desc, R G].  P is the bin count
  * the map was planned with (it fixes the layout offsets).
  * ([HPC-Ops] "Scheduling around live KV work": each workgroup writes a
  * partial output with its log-sum-exp for every descriptor it drains). */
@@ -394,6 +436,7 @@ int orc_partials(const orc_dims *dm, const void *q, const float *q_scale,
     const int B = map[5], H_kv = map[6];
     const int G = dm->num_q_heads / dm->num_kv_heads;
     const int D = dm->head_dim;
+    const int R = rows_of(dm);
     const int64_t nd = map[4];
     const int64_t S = (int64_t)B * H_kv;
     const int32_t *lens = map + 8;
@@ -405,18 +448,17 @@ int orc_partials(const orc_dims *dm, const void *q, const float *q_scale,
         int b = d4[0], h = d4[1];
         int tok0 = d4[2] * ORC_TILE;
         int tok1 = d4[3] * ORC_TILE;
-        if (tok1 > lens[b])
-            tok1 = lens[b];
         err |= orc_attend_range(dm, q, q_scale, k_pages, v_pages, k_scale, v_scale,
-                                page_table, b, h, tok0, tok1,
-                                part_o + k * G * D, part_lse + k * G);
+                                page_table, b, h, tok0, tok1, lens[b],
+                                part_o + k * R * G * D, part_lse + k * R * G);
     }
     return err ? -1 : 0;
 }
 
 /* Merge the partials of each segment (its descriptors are the contiguous
- * run seg_desc_off[s] .. seg_desc_off[s + 1]) into out [B, H_q, D] and
- * out_lse [B, H_q].  P is the bin count the map was planned with. */
+ * run seg_desc_off[s] .. seg_desc_off[s + 1]), row by row, into
+ * out [B, R, H_q, D] and out_lse [B, R, H_q].  P is the bin count the map
+ * was planned with. */
 int orc_combine(const orc_dims *dm, const int32_t *map, int32_t P,
                 const double *part_o, const double *part_lse,
                 double *out, double *out_lse)
@@ -424,6 +466,7 @@ int orc_combine(const orc_dims *dm, const int32_t *map, int32_t P,
     const int B = map[5], H_kv = map[6];
     const int G = dm->num_q_heads / dm->num_kv_heads;
     const int D = dm->head_dim;
+    const int R = rows_of(dm);
     const int64_t S = (int64_t)B * H_kv;
     const int32_t *seg_off = map + 8 + B + (P + 1);
     int err = 0;
@@ -440,13 +483,13 @@ int orc_combine(const orc_dims *dm, const int32_t *map, int32_t P,
             err |= 1;
             continue;
         }
-        for (int g = 0; g < G; ++g) {
+        for (int c = 0; c < R * G; ++c) {
             for (int i = 0; i < n; ++i) {
-                lse[i] = part_lse[(int64_t)(k0 + i) * G + g];
-                memcpy(og + (int64_t)i * D, part_o + ((int64_t)(k0 + i) * G + g) * D,
+                lse[i] = part_lse[(int64_t)(k0 + i) * R * G + c];
+                memcpy(og + (int64_t)i * D, part_o + ((int64_t)(k0 + i) * R * G + c) * D,
                        sizeof(double) * D);
             }
-            int64_t row = (int64_t)b * dm->num_q_heads + (int64_t)h * G + g;
+            int64_t row = ((int64_t)b * R + c / G) * dm->num_q_heads + (int64_t)h * G + c % G;
             orc_lse_merge(n, D, lse, og, out + row * D, out_lse + row);
         }
         free(lse);
