@@ -5,7 +5,8 @@ once, then hpcattn_decode + hpcattn_combine for every layer, each layer with
 its own KV pool (so the 256 MB Infinity Cache cannot serve repeats).  Inputs
 are resident in HBM before the timed region starts.
 
-    python bench.py [--steps K] [--warmup W] [--workload mixed|single_long|heavy_tail|fp8]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload mixed|single_long|heavy_tail|fp8|mtp|mtp_fp8|prologue]
                     [--num-bins P] [--min-tiles m] [--ablation] [--no-cpu-baseline]
 
 Prints one JSON line.  `value` is the step's KV-read throughput (live KV
@@ -46,6 +47,14 @@ DESCRIPTIONS = {
     "fp8": "fp8 KV: 32 requests, KV lens log-uniform in [1024, 131072], 8 KV / 64 Q heads, "
            "head_dim 128, e4m3 Q/K/V with per-token per-head fp32 scales, page 64, "
            "4 rotating KV pools",
+    "mtp": "draft verify: the mixed-length batch (64 requests, KV lens log-uniform in "
+           "[256, 32768], seed 0) with 6 query rows per request (1 + 5 drafts, causal among "
+           "themselves), 8 KV / 64 Q heads, head_dim 128, bf16, page 64, 32 layers with "
+           "distinct KV pools, one task map per step",
+    "mtp_fp8": "draft verify, fp8 KV: the fp8 batch (32 requests, KV lens log-uniform in "
+               "[1024, 131072]) with 6 query rows per request (1 + 5 drafts), 8 KV / 64 Q "
+               "heads, head_dim 128, e4m3 Q/K/V with per-token per-head fp32 scales, page 64, "
+               "4 rotating KV pools",
 }
 
 
@@ -343,8 +352,9 @@ def main():
     torch.cuda.set_device(0)
     name = args.workload
     w = wl.WORKLOADS[name]
-    layers = args.layers if args.layers is not None else (w.layers if name == "mixed" else 1)
-    pools = layers if name == "mixed" else max(1, args.pools)
+    multi_layer = w.layers > 1
+    layers = args.layers if args.layers is not None else (w.layers if multi_layer else 1)
+    pools = layers if multi_layer else max(1, args.pools)
     prob = wl.make_problem(name, seed=args.seed, device="cuda", layers=pools)
     run = runner.DecodeRunner(prob, num_bins=args.num_bins, min_tiles=args.min_tiles)
     stream = torch.cuda.current_stream()
@@ -415,7 +425,7 @@ def main():
     wall = time.perf_counter() - wall0
 
     # Per-kernel GPU time, each kernel back to back in its own graph.
-    n_dec = max(layers, pools) if name == "mixed" else pools
+    n_dec = max(layers, pools) if multi_layer else pools
     dec_avg = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec)
     combine_ms = graph_avg_ms(lambda: [run.combine() for _ in range(16)], 16)
     plan_ms = graph_avg_ms(lambda: [run.plan() for _ in range(16)], 16)
@@ -448,6 +458,7 @@ def main():
             "min_tiles": run.min_tiles,
             "num_desc": run.num_desc(),
             "seed": args.seed,
+            "q_rows": w.q_rows,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "breakdown_us": {"plan": round(plan_ms * 1e3, 2),
@@ -467,10 +478,51 @@ def main():
 
     if args.ablation:
         out["ablation"] = static_sweep(run, prob, layers, pools, stream, dec_avg)
+    if w.q_rows > 1:
+        out["multi_row"] = rows_as_requests(prob, layers, pools, med_step, dec_avg, capture,
+                                            graph_avg_ms, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def rows_as_requests(prob, layers, pools, step_ms, dec_ms, capture, graph_avg_ms, args):
+    """The same draft-verify step done by a decode that takes one query row
+    per request: each of the R rows of request b becomes a request of its own
+    over the first L_b - (R - 1 - r) tokens (same page-table row, same KV
+    pools, same query bytes), planned and combined as B R requests."""
+    import numpy as np
+
+    from load_balanced_split_amd import runner, workloads as wl
+
+    w, R = prob.workload, prob.workload.q_rows
+    B = prob.seq_lens.shape[0]
+    lens = np.repeat(prob.seq_lens, R) - np.tile(np.arange(R - 1, -1, -1), B)
+    one = wl.Workload(w.name + "_rows", None, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                      w.kv_dtype, layers=w.layers, num_bins=w.num_bins, min_tiles=w.min_tiles)
+    flat = wl.Problem(one, np.maximum(lens, 0).astype(np.int32),
+                      np.repeat(prob.page_table, R, axis=0), prob.num_pages,
+                      prob.q.view(B * R, w.num_q_heads, w.head_dim), prob.k_pages, prob.v_pages,
+                      None if prob.q_scale is None else prob.q_scale.view(B * R, w.num_q_heads),
+                      prob.k_scale, prob.v_scale, prob.sm_scale)
+    run = runner.DecodeRunner(flat, num_bins=args.num_bins, min_tiles=args.min_tiles)
+
+    def step():
+        run.plan()
+        for layer in range(layers):
+            run.decode(layer % pools)
+            run.combine()
+
+    step()
+    per = graph_avg_ms(step, 1, reps=max(2, min(10, args.steps)))
+    n_dec = max(layers, pools)
+    dec = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec)
+    return {"rows": R,
+            "rows_as_requests_us_per_step": round(per * 1e3, 1),
+            "rows_as_requests_decode_avg_us": round(dec * 1e3, 2),
+            "speedup_vs_rows_as_requests": round(per / step_ms, 3),
+            "decode_speedup_vs_rows_as_requests": round(dec / dec_ms, 3)}
 
 
 def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8):

@@ -20,6 +20,16 @@
  *   hpcattn_static_decode is the static split-KV scheme the pages compare
  *   against (fixed split count, or fixed chunk size), for ablation.
  *
+ * Multi-row decode ("Hy3 preview full-stack inference optimization", section
+ * 2.5, MTP; "SGLang Low-Latency Mode: Kernels and Runtime", section 1: a
+ * verify step checks the confirmed token and the draft tokens of a request
+ * in one forward): with q_rows = R > 1 each request brings R query rows, the
+ * last R tokens of the request, which the cache already holds.  Row r sits
+ * at position L_b - R + r and attends to tokens [0, L_b - R + r] (a causal
+ * mask among the rows; the pages give none, this is the plain reading of
+ * verifying a token sequence).  The plan and its task map do not change:
+ * one K/V tile serves all R G rows of its KV head.  R = 1 is plain decode.
+ *
  * Conventions (all entry points):
  *   - Every pointer argument is a DEVICE pointer unless marked "host".
  *   - The caller owns every buffer.  The library allocates, frees and caches
@@ -30,18 +40,20 @@
  *     are detected on the host before anything is enqueued; a launch error
  *     reported by the runtime returns HPCATTN_ERR_LAUNCH.
  *   - Layouts are row-major and contiguous:
- *       q           [B, H_q, D]              bf16, or e4m3 bytes
- *       q_scale     [B, H_q]                 fp32 (fp8 only)
+ *       q           [B, R, H_q, D]           bf16, or e4m3 bytes
+ *       q_scale     [B, R, H_q]              fp32 (fp8 only)
  *       k_pages     [num_pages, H_kv, 64, D] bf16, or e4m3 bytes
  *       v_pages     [num_pages, H_kv, 64, D] same type as k_pages
  *       k_scale     [num_pages, H_kv, 64]    fp32 (fp8 only); v_scale likewise
  *       page_table  [B, max_pages_per_req]   int32; token t of request b sits
  *                   in slot t % 64 of page page_table[b][t / 64]
- *       part_o      [max_partials, G, D]     fp32, normalised partial output
- *       part_lse    [max_partials, G]        fp32, natural-log LSE of the
+ *       part_o      [max_partials, R G, D]   fp32, normalised partial output;
+ *                   row r G + g is query row r, head h G + g
+ *       part_lse    [max_partials, R G]      fp32, natural-log LSE of the
  *                   scaled logits of the partial's tokens
- *       out         [B, H_q, D]              bf16 (round to nearest even)
- *       out_lse     [B, H_q]                 fp32, natural log
+ *       out         [B, R, H_q, D]           bf16 (round to nearest even)
+ *       out_lse     [B, R, H_q]              fp32, natural log
+ *     R = q_rows (the R axis is absent in effect when R = 1);
  *     G = H_q / H_kv; query head j reads KV head j / G.  fp8 is OCP E4M3FN
  *     and a value is code * scale.
  *   - Data errors (a length beyond 64 * max_pages_per_req, a page id outside
@@ -61,6 +73,7 @@ extern "C" {
 #define HPCATTN_PAGE_SIZE 64   /* tokens per KV page and per tile            */
 #define HPCATTN_MAX_BATCH 8192 /* requests per plan                          */
 #define HPCATTN_MAX_GROUP 16   /* query heads per KV head                     */
+#define HPCATTN_MAX_ROWS 64    /* query rows per KV head, q_rows * G          */
 
 typedef enum {
     HPCATTN_OK = 0,
@@ -91,6 +104,8 @@ typedef struct {
     int32_t num_pages;          /* pages in k_pages / v_pages                  */
     int32_t kv_dtype;           /* hpcattn_kv_dtype                            */
     float sm_scale;             /* softmax scale on q . k, e.g. 1/sqrt(D)      */
+    int32_t q_rows;             /* R >= 1 query rows per request (1 + drafts); */
+                                /* q_rows * G <= HPCATTN_MAX_ROWS              */
 } hpcattn_dims;
 
 /*
@@ -129,12 +144,13 @@ int64_t hpcattn_max_partials(int32_t batch, int32_t num_kv_heads, int32_t num_bi
 /*
  * The number of decode workgroups that are co-resident on the current device
  * (compute units x workgroups per CU at the kernel's register and LDS use)
- * for this head_dim, kv_dtype and group size G: the natural num_bins, one
+ * for this head_dim, kv_dtype and rows = q_rows * G query rows per KV head
+ * (G for plain decode): the natural num_bins, one
  * persistent workgroup per bin with no second round.  A host query (reads
  * device attributes, enqueues nothing).  Returns > 0, or HPCATTN_ERR_ARG for
  * an unsupported shape, HPCATTN_ERR_LAUNCH if the runtime cannot answer.
  */
-int32_t hpcattn_suggest_num_bins(int32_t head_dim, int32_t kv_dtype, int32_t group);
+int32_t hpcattn_suggest_num_bins(int32_t head_dim, int32_t kv_dtype, int32_t rows);
 
 /*
  * The assign step ("Scheduling around live KV work"; "Attention dynamic

@@ -29,7 +29,8 @@ int check_dims(const hpcattn_dims *d) {
         d->num_q_heads < d->num_kv_heads || d->num_q_heads % d->num_kv_heads != 0 ||
         d->num_q_heads / d->num_kv_heads > HPCATTN_MAX_GROUP ||
         (d->head_dim != 64 && d->head_dim != 128) || d->max_pages_per_req < 1 ||
-        d->num_pages < 1)
+        d->num_pages < 1 || d->q_rows < 1 ||
+        d->q_rows * (d->num_q_heads / d->num_kv_heads) > HPCATTN_MAX_ROWS)
         return HPCATTN_ERR_SHAPE;
     if (d->kv_dtype != HPCATTN_KV_BF16 && d->kv_dtype != HPCATTN_KV_FP8_E4M3)
         return HPCATTN_ERR_DTYPE;
@@ -68,6 +69,7 @@ DecodeParams make_params(const hpcattn_dims *d, const void *q, const float *q_sc
     p.G = d->num_q_heads / d->num_kv_heads;
     p.max_pages = d->max_pages_per_req;
     p.num_pages = d->num_pages;
+    p.R = d->q_rows;
     p.scale_log2 = d->sm_scale * kLog2e;
     return p;
 }
@@ -161,18 +163,21 @@ int hpcattn_combine(const hpcattn_dims *dims, const hpcattn_task_map *map,
     c.S = dims->batch * dims->num_kv_heads;
     c.G = dims->num_q_heads / dims->num_kv_heads;
     c.D = dims->head_dim;
+    c.R = dims->q_rows;
+    c.Hkv = dims->num_kv_heads;
+    c.max_chunks = hpcattn_max_partials(map->batch, map->num_kv_heads, map->num_bins);
     return launch_status(launch_combine(c, (hipStream_t)stream));
 }
 
-int32_t hpcattn_suggest_num_bins(int32_t head_dim, int32_t kv_dtype, int32_t group) {
-    if ((head_dim != 64 && head_dim != 128) || group < 1 || group > HPCATTN_MAX_GROUP ||
+int32_t hpcattn_suggest_num_bins(int32_t head_dim, int32_t kv_dtype, int32_t rows) {
+    if ((head_dim != 64 && head_dim != 128) || rows < 1 || rows > HPCATTN_MAX_ROWS ||
         (kv_dtype != HPCATTN_KV_BF16 && kv_dtype != HPCATTN_KV_FP8_E4M3))
         return HPCATTN_ERR_ARG;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return HPCATTN_ERR_LAUNCH;
-    const int32_t per_cu = decode_resident_per_cu(head_dim, kv_dtype, group);
+    const int32_t per_cu = decode_resident_per_cu(head_dim, kv_dtype, rows);
     if (per_cu < 1 || cus < 1) return HPCATTN_ERR_LAUNCH;
     return per_cu * cus;
 }
@@ -219,6 +224,8 @@ int hpcattn_static_decode(const hpcattn_dims *dims, int32_t policy, int32_t para
     c.S = dims->batch * dims->num_kv_heads;
     c.G = p.G;
     c.D = dims->head_dim;
+    c.R = dims->q_rows;
+    c.Hkv = dims->num_kv_heads;
     return launch_status(launch_combine(c, (hipStream_t)stream));
 }
 
@@ -290,6 +297,6 @@ const char *hpcattn_strerror(int status) {
     }
 }
 
-int hpcattn_version(void) { return 100; }
+int hpcattn_version(void) { return 200; }
 
 }  // extern "C"

@@ -11,17 +11,22 @@
 //   M = max_k lse_k,  w_k = exp(lse_k - M),
 //   out = sum_k w_k o_k / sum_k w_k,  out_lse = M + ln sum_k w_k.
 //
-// One workgroup of 4 waves per (segment, query head of its group).  Wave w
-// merges chunks w, w + 4, ... in one pass with a running maximum (each lane
-// owns D/64 consecutive elements of the row, so a chunk's row is one
-// coalesced 512-byte read), four chunks' loads in flight per wave; the four
-// waves are then merged in LDS.  A chunk with lse = -inf (an empty static
-// split) carries no weight and its row is never read.
+// With R query rows per request (draft verify), a segment's partials hold
+// R G rows each, row r G + g for query row r and head h G + g, and every row
+// is merged on its own.
+//
+// A workgroup of 4 waves merges 4 / WPR rows of one segment, WPR waves per
+// row.  Wave k of a row merges chunks k, k + WPR, ... in one pass with a
+// running maximum (each lane owns D/64 consecutive elements of the row, so a
+// chunk's row is one coalesced read), four chunks' loads in flight per wave;
+// with WPR > 1 the row's waves are then merged in LDS.  WPR = 4 suits
+// segments cut into many chunks (a long request over many bins), WPR = 1
+// segments of a few chunks with many rows.  A chunk with lse = -inf (an
+// empty static split) carries no weight and its row is never read.
 #include "common.h"
 
 namespace hpcattn {
 namespace {
-
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -45,16 +50,18 @@ struct Merge {
     }
 };
 
-template <int D>
+template <int D, int WPR>
 __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
-    constexpr int E = D / 64;   // elements per lane
+    constexpr int E = D / 64;            // elements per lane
+    constexpr int RPW = kWaves / WPR;    // rows per workgroup
     __shared__ float s_m[kWaves], s_w[kWaves];
     __shared__ float s_acc[kWaves][D];
 
     const int64_t s = blockIdx.x;
-    const int g = blockIdx.y;
-    const int G = p.G;
+    const int G = p.G, RG = p.R * p.G;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c = blockIdx.y * RPW + w / WPR;   // partial row r G + g
+    const int part = w % WPR;
     int64_t k0, k1;
     if (p.seg_off) {
         k0 = p.seg_off[s];
@@ -63,16 +70,16 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
         k0 = s * p.stride;
         k1 = k0 + p.stride;
     }
-    const int64_t n = k1 - k0;
+    const int64_t n = c < RG ? k1 - k0 : 0;   // rows past R G (last workgroup) merge nothing
 
     Merge<E> mg;
-    for (int64_t k = w; k < n; k += kWaves * kUnroll) {
+    for (int64_t k = part; k < n; k += WPR * kUnroll) {
         float l[kUnroll];
         float o[kUnroll][E];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t kk = k + u * kWaves;
-            const int64_t row = (k0 + (kk < n ? kk : k)) * G + g;
+            const int64_t kk = k + u * WPR;
+            const int64_t row = (k0 + (kk < n ? kk : k)) * RG + c;
             l[u] = kk < n ? p.part_lse[row] : kNegInf;
             const float *src = p.part_o + row * D + lane * E;
 #pragma unroll
@@ -81,19 +88,23 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) mg.add(l[u], o[u]);
     }
-    if (lane == 0) {
-        s_m[w] = mg.M;
-        s_w[w] = mg.W;
-    }
+    if constexpr (WPR > 1) {
+        if (lane == 0) {
+            s_m[w] = mg.M;
+            s_w[w] = mg.W;
+        }
 #pragma unroll
-    for (int e = 0; e < E; ++e) s_acc[w][lane * E + e] = mg.acc[e];
-    __syncthreads();
-    if (w != 0) return;
+        for (int e = 0; e < E; ++e) s_acc[w][lane * E + e] = mg.acc[e];
+        __syncthreads();
+    }
+    if (part != 0 || c >= RG) return;
 
     float M = kNegInf;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i]);
-    const int64_t out_row = s * G + g;
+    for (int i = 0; i < WPR; ++i) M = fmaxf(M, WPR > 1 ? s_m[w + i] : mg.M);
+    // out [B, R, H_q, D]: request b = s / Hkv, KV head h = s % Hkv
+    const int64_t out_row =
+        ((s / p.Hkv) * p.R + c / G) * (int64_t)(p.Hkv * G) + (s % p.Hkv) * G + c % G;
     __bf16 *out = reinterpret_cast<__bf16 *>(p.out) + out_row * D + lane * E;
     if (M == kNegInf) {   // no live KV: out = 0, lse = -inf
 #pragma unroll
@@ -102,12 +113,18 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
         return;
     }
     float W = 0.f, acc[E] = {};
+    if constexpr (WPR > 1) {
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        const float c = s_m[i] == kNegInf ? 0.f : __expf(s_m[i] - M);
-        W += c * s_w[i];
+        for (int i = 0; i < WPR; ++i) {
+            const float cm = s_m[w + i] == kNegInf ? 0.f : __expf(s_m[w + i] - M);
+            W += cm * s_w[w + i];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += c * s_acc[i][lane * E + e];
+            for (int e = 0; e < E; ++e) acc[e] += cm * s_acc[w + i][lane * E + e];
+        }
+    } else {
+        W = mg.W;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = mg.acc[e];
     }
     const float inv = 1.0f / W;
 #pragma unroll
@@ -115,15 +132,27 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
     if (p.out_lse && lane == 0) p.out_lse[out_row] = M + __logf(W);
 }
 
+template <int D, int WPR>
+void launch(const CombineParams &p, hipStream_t stream) {
+    constexpr int RPW = kWaves / WPR;
+    const int rows = p.R * p.G;
+    const dim3 grid((unsigned)p.S, (unsigned)((rows + RPW - 1) / RPW));
+    hipLaunchKernelGGL((combine_kernel<D, WPR>), grid, dim3(kThreads), 0, stream, p);
+}
+
 }  // namespace
 
+// Waves per row from the mean chunk count of a segment: the dynamic map has
+// at most S + P - 1 descriptors over S segments; a static split has `stride`.
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream) {
     if (p.S <= 0) return hipSuccess;
-    const dim3 grid((unsigned)p.S, (unsigned)p.G);
-    if (p.D == 128)
-        hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+    const int64_t chunks = p.seg_off ? (p.S + p.max_chunks - 1) / p.S : p.stride;
+    const bool many = chunks >= 8;
+    if (p.D == 128) {
+        if (many) launch<128, 4>(p, stream); else launch<128, 1>(p, stream);
+    } else {
+        if (many) launch<64, 4>(p, stream); else launch<64, 1>(p, stream);
+    }
     return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ struct DecodeParams {
     const int32_t *map;
     const int32_t *seq_lens;
     int32_t B, Hq, Hkv, G, max_pages, num_pages;
+    int32_t R;              // query rows per request (1 + draft tokens)
     int32_t P;              // bins (dynamic)
     int32_t policy, param;  // static split policy and its parameter
     int32_t splits;         // static: slots per segment
@@ -56,6 +57,8 @@ struct CombineParams {
     void *out;
     float *out_lse;
     int32_t S, G, D;
+    int32_t R, Hkv;          // query rows per request; segment s = b * Hkv + h
+    int64_t max_chunks;      // with seg_off: partial slots of the map (S + P - 1)
 };
 
 // Arguments of the prologue kernel.
@@ -85,7 +88,8 @@ hipError_t launch_static_decode(const DecodeParams &p, int32_t head_dim, int32_t
                                 hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 hipError_t launch_prologue(const PrologueParams &p, int32_t head_dim, hipStream_t stream);
-int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t group);
+// rows = R * G, the query rows that share one KV head's tiles.
+int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t rows);
 hipError_t launch_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
                               uint32_t *sink, hipStream_t stream);
 

@@ -13,9 +13,12 @@
 //   * a workgroup is 4 waves; wave w owns tokens [16 w, 16 w + 16) of every
 //     tile, so all 4 waves stay busy even on one-tile descriptors and no
 //     barrier is needed inside a descriptor;
-//   * one K/V tile (64 tokens of one KV head) serves all G <= 16 query heads
-//     of its group: S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,fp8} (16 tokens
-//     x 16 head columns, G used), O^T += V^T P^T on v_mfma_f32_16x16x16_bf16;
+//   * one K/V tile (64 tokens of one KV head) serves every query row of its
+//     group: the G query heads times the R rows of a multi-row (draft
+//     verify) step, R G <= 64, as NCB = ceil(R G / 16) blocks of 16 columns:
+//     S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,fp8} (16 tokens x 16
+//     columns per block), O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, the K
+//     and V operands shared by all blocks;
 //   * K and V go straight from HBM to registers with 16-byte loads: lane
 //     (r = lane % 16, grp = lane / 16) reads token 16 w + r of K at a d-range
 //     that only has to match Q's, and tokens 16 w + 4 grp + j of V at
@@ -54,6 +57,13 @@ struct Lane {
         grp = lane >> 4;
     }
 };
+
+// Query rows per request: MR (multi-row) kernels read R from the arguments,
+// the others are compiled for R = 1.
+template <bool MR>
+__device__ __forceinline__ int rows_per_req(const DecodeParams &p) {
+    return MR ? p.R : 1;
+}
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -151,6 +161,44 @@ struct Bf16 {
 
     static constexpr bool kScaled = false;
 
+    // Shared-tile path (K and V rows in LDS).  Raw Q K^T of 16 tokens from
+    // the lane's KC 16-byte K chunks (chunk i at byte 64 i + 16 grp of its
+    // token's row: the d-range of k-step i).
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int KC = D / 32;
+    __device__ static f32x4 qk(const u32x4 (&k)[KC], const Q &q) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, k[ks]), __builtin_bit_cast(bf16x8, q.q[ks]), acc,
+                0, 0, 0);
+        return acc;
+    }
+    // The lane's D/16 V values of one token (d = r D/16 ..) as bf16 pairs.
+    __device__ static void v_row(const uint8_t *row, const Lane &ln, uint32_t (&w)[VW]) {
+        const uint8_t *src = row + ln.r * (D / 16) * 2;
+        if constexpr (VW == 4) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(src);
+            w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+        } else {
+            const u32x2 x = *reinterpret_cast<const u32x2 *>(src);
+            w[0] = x[0]; w[1] = x[1];
+        }
+    }
+
+    // Dwords c0 .. c0 + N - 1 of the lane's V run of one token.
+    template <int N>
+    __device__ static void v_part(const uint8_t *row, const Lane &ln, int c0, uint32_t (&w)[N]) {
+        const uint8_t *src = row + ln.r * (D / 16) * 2 + 4 * c0;
+        if constexpr (N == 2) {
+            const u32x2 x = *reinterpret_cast<const u32x2 *>(src);
+            w[0] = x[0]; w[1] = x[1];
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t *>(src);
+        }
+    }
+
     // V^T operand of d-block blk: {V[t_j][r * D/16 + blk], j < 4} as bf16.
     __device__ static void v_dwords(const Tile &t, uint32_t (&vv)[4][VW]) {
 #pragma unroll
@@ -226,6 +274,55 @@ struct Fp8 {
 
     static constexpr bool kScaled = true;
 
+    // Shared-tile path: raw Q K^T of 16 tokens from the lane's KC 16-byte K
+    // chunks (chunk c at byte 64 c + 16 grp: k-steps 2 c and 2 c + 1).
+    static constexpr int kRowBytes = D;
+    static constexpr int KC = D / 64;
+    __device__ static f32x4 qk(const u32x4 (&k)[KC], const Q &q) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c = ks >> 1, sub = ks & 1;
+            const long a = __builtin_bit_cast(long, u32x2{k[c][2 * sub], k[c][2 * sub + 1]});
+            const long b = __builtin_bit_cast(long, u32x2{q.q[c][2 * sub], q.q[c][2 * sub + 1]});
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, acc, 0, 0, 0);
+        }
+        return acc;
+    }
+    // The lane's D/16 V values of one token (d = r D/16 ..) widened to bf16.
+    __device__ static void v_row(const uint8_t *row, const Lane &ln, uint32_t (&w)[VW]) {
+        const uint8_t *src = row + ln.r * (D / 16);
+        uint32_t x[VB];
+        if constexpr (VB == 2) {
+            const u32x2 y = *reinterpret_cast<const u32x2 *>(src);
+            x[0] = y[0]; x[1] = y[1];
+        } else {
+            x[0] = *reinterpret_cast<const uint32_t *>(src);
+        }
+#pragma unroll
+        for (int c = 0; c < VB; ++c) {
+            w[2 * c] = __builtin_bit_cast(uint32_t,
+                                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[c], 1.0f, false));
+            w[2 * c + 1] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[c], 1.0f, true));
+        }
+    }
+
+    // Dwords c0 .. c0 + N - 1 of the lane's widened V run of one token
+    // (dword c holds fp8 bytes 2 c, 2 c + 1 of the run as bf16).
+    template <int N>
+    __device__ static void v_part(const uint8_t *row, const Lane &ln, int c0, uint32_t (&w)[N]) {
+        const uint8_t *src = row + ln.r * (D / 16) + 2 * c0;
+        if constexpr (N == 2) {
+            const uint32_t x = *reinterpret_cast<const uint32_t *>(src);
+            w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+            w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+        } else {
+            const uint32_t x = *reinterpret_cast<const uint16_t *>(src);
+            w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+        }
+    }
+
     // Widen each token's D/16 fp8 values to bf16 (exact: every e4m3 value is
     // a bf16 value).
     __device__ static void v_dwords(const Tile &t, uint32_t (&vv)[4][VW]) {
@@ -245,62 +342,83 @@ struct Fp8 {
 // Per-wave online-softmax state and the 4-wave merge.
 // ---------------------------------------------------------------------------
 
-template <int D>
+template <int D, int NCB>
 struct State {
     static constexpr int NB = D / 16;   // 16-wide d-blocks of O^T
-    f32x4 o[NB];   // O[g = r][d = (4 grp + i) * D/16 + blk] for blk, i
-    float m, l;    // running max (log2 units) and sum for head g = r
+    f32x4 o[NCB][NB];   // O[column 16 cb + r][d = (4 grp + i) * D/16 + blk]
+    float m[NCB], l[NCB];   // running max (log2 units) and sum of that column
 
     __device__ void reset() {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m = kNegInf;
-        l = 0.f;
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) o[cb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m[cb] = kNegInf;
+            l[cb] = 0.f;
+        }
     }
 };
 
-// One tile's share for this wave: nv = live tokens of the tile (0 .. 64).
-template <class KV, int D>
-__device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_t *sq,
-                                            float qs, const typename KV::Tile &t, int nv,
-                                            State<D> &st, const Lane &ln) {
-    typename KV::Q q;
-    KV::read_q(sq, KV::kQRowBytes / 4 + 4, ln, q);
-    f32x4 s = KV::scores(p, q, t, qs, 0, 0, ln);
-    const int tok0 = 16 * ln.w + 4 * ln.grp;
-    if (nv < kTile) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tok0 + i >= nv) s[i] = kNegInf;
-    }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // The reference max st.m moves only when a tile's max exceeds it by more
-    // than kSlack (log2 units), so weights stay <= 2^kSlack and O, l are
-    // rescaled (a wave-uniform branch) only on those rare tiles.
-    if (__any(mx > st.m + kSlack)) {
-        const bool moves = mx > st.m + kSlack;
-        const float m_new = moves ? mx : st.m;
-        // 1 where the reference is kept (also when it stays -inf), 0 from -inf
-        const float alpha = moves ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
-        st.l *= alpha;
-#pragma unroll
-        for (int b = 0; b < D / 16; ++b) st.o[b] = st.o[b] * alpha;
-        st.m = m_new;
-    }
-    const float m_use = st.m == kNegInf ? 0.f : st.m;
-    f32x4 pr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-    float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    st.l += ps;
+// Per-lane constants of the query columns 16 cb + r of a workgroup: column c
+// is query row c / G (of R) and head c % G.  A row r sees R - 1 - r fewer
+// tokens than the request holds (causal mask among the draft rows).
+template <int NCB>
+struct Cols {
+    int lag[NCB];    // R - 1 - row, 0 for the padding columns c >= R G
+    int qoff[NCB];   // row * H_q + head, the column's offset in q_scale
+};
 
-    if constexpr (KV::kScaled) pr = pr * t.vs;   // fold the per-token V scale into P
-    const s16x4 pb = __builtin_bit_cast(
-        s16x4, u32x2{pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])});
+// One tile's share for this wave: nv = tokens of the request from the
+// tile's first on (live tokens of the tile for nv < 64); the query rows of a
+// column see nv - lag of them.
+template <class KV, int D, int NCB, bool MR>
+__device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_t *sq,
+                                            const float (&qs)[NCB], const typename KV::Tile &t,
+                                            int nv, const Cols<NCB> &cols, State<D, NCB> &st,
+                                            const Lane &ln) {
+    constexpr int QS = KV::kQRowBytes / 4 + 4;   // LDS Q row stride in dwords
+    const int tok0 = 16 * ln.w + 4 * ln.grp;
+    s16x4 pb[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        typename KV::Q q;
+        KV::read_q(sq + 16 * cb * QS, QS, ln, q);
+        f32x4 s = KV::scores(p, q, t, qs[cb], 0, 0, ln);
+        if (nv - (rows_per_req<MR>(p) - 1) < kTile) {   // a row sees < 64 of the tile
+            const int lim = nv - cols.lag[cb];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tok0 + i >= lim) s[i] = kNegInf;
+        }
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // The reference max moves only when a tile's max exceeds it by more
+        // than kSlack (log2 units), so weights stay <= 2^kSlack and O, l are
+        // rescaled (a wave-uniform branch) only on those rare tiles.
+        if (__any(mx > st.m[cb] + kSlack)) {
+            const bool moves = mx > st.m[cb] + kSlack;
+            const float m_new = moves ? mx : st.m[cb];
+            // 1 where the reference is kept (also when it stays -inf), 0 from -inf
+            const float alpha = moves ? __builtin_amdgcn_exp2f(st.m[cb] - m_new) : 1.f;
+            st.l[cb] *= alpha;
+#pragma unroll
+            for (int b = 0; b < D / 16; ++b) st.o[cb][b] = st.o[cb][b] * alpha;
+            st.m[cb] = m_new;
+        }
+        const float m_use = st.m[cb] == kNegInf ? 0.f : st.m[cb];
+        f32x4 pr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+        float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        st.l[cb] += ps;
+
+        if constexpr (KV::kScaled) pr = pr * t.vs;   // fold the per-token V scale into P
+        pb[cb] = __builtin_bit_cast(s16x4,
+                                    u32x2{pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])});
+    }
 
     uint32_t vv[4][D / 32];
     KV::v_dwords(t, vv);
@@ -316,77 +434,94 @@ __device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_
         // d-blocks 2c and 2c + 1: low and high bf16 of dword c of each token.
         const u32x2 lo = {halves<false>(vv[0][c], vv[1][c]), halves<false>(vv[2][c], vv[3][c])};
         const u32x2 hi = {halves<true>(vv[0][c], vv[1][c]), halves<true>(vv[2][c], vv[3][c])};
-        st.o[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(s16x4, lo), pb, st.o[2 * c], 0, 0, 0);
-        st.o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(s16x4, hi), pb, st.o[2 * c + 1], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            st.o[cb][2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s16x4, lo), pb[cb], st.o[cb][2 * c], 0, 0, 0);
+            st.o[cb][2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s16x4, hi), pb[cb], st.o[cb][2 * c + 1], 0, 0, 0);
+        }
     }
 }
 
-// LDS scratch for merging the 4 waves of a workgroup.
-template <int D, int GR>
+// LDS scratch for merging the 4 waves of a workgroup, one 16-column block
+// at a time (GR = 8 when a workgroup has at most 8 columns).
+template <int D, int GR, int NCB>
 struct MergeLds {
     float o[kWaves][GR][D];
     float m[kWaves][GR];
     float l[kWaves][GR];
-    // The current descriptor's Q rows (16 rows, rows >= G zero), each padded
-    // by 4 dwords so that the per-tile operand reads are bank-conflict free.
-    uint32_t q[16 * (D / 2 + 4)];
+    // The current descriptor's Q rows (16 NCB rows, rows >= R G zero), each
+    // padded by 4 dwords so that the per-tile operand reads are bank-conflict
+    // free.
+    uint32_t q[16 * NCB * (D / 2 + 4)];
 };
 
-// Copy the G query rows of (b, h) into the LDS Q rows.  All threads.
-template <class KV, int D, int GR>
-__device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR> &sm, int b,
+// Copy the R G query rows of (b, h) into the LDS Q rows: LDS row r G + g is
+// query row r, head h G + g (the G heads of one row are contiguous in q).
+// All threads.
+template <class KV, int D, int GR, int NCB, bool MR>
+__device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR, NCB> &sm, int b,
                                         int h) {
     constexpr int RW = KV::kQRowBytes / 4, QS = RW + 4;
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(
-        reinterpret_cast<const char *>(p.q) +
-        ((int64_t)b * p.Hq + (int64_t)h * p.G) * KV::kQRowBytes);
-    for (int i = threadIdx.x; i < p.G * RW; i += kDecodeThreads)
-        sm.q[(i / RW) * QS + i % RW] = src[i];
+    const int R = rows_per_req<MR>(p);
+    for (int r = 0; r < R; ++r) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(
+            reinterpret_cast<const char *>(p.q) +
+            (((int64_t)b * R + r) * p.Hq + (int64_t)h * p.G) * KV::kQRowBytes);
+        uint32_t *dst = sm.q + r * p.G * QS;
+        for (int i = threadIdx.x; i < p.G * RW; i += kDecodeThreads)
+            dst[(i / RW) * QS + i % RW] = src[i];
+    }
 }
 
-// Merge the waves' states and write partial slot `slot`.  All threads.
-template <int D, int GR, class Between>
-__device__ __forceinline__ void merge_write(const DecodeParams &p, State<D> &st,
-                                            MergeLds<D, GR> &sm, int64_t slot, const Lane &ln,
-                                            Between between) {
-    const int G = p.G;
-    if (ln.r < G) {
-        if (ln.grp == 0) {
-            sm.m[ln.w][ln.r] = st.m;
-            sm.l[ln.w][ln.r] = st.l;
-        }
+// Merge the waves' states and write partial slot `slot` (R G rows).  All
+// threads.
+template <int D, int GR, int NCB, bool MR, class Between>
+__device__ __forceinline__ void merge_write(const DecodeParams &p, State<D, NCB> &st,
+                                            MergeLds<D, GR, NCB> &sm, int64_t slot,
+                                            const Lane &ln, Between between) {
+    const int RG = rows_per_req<MR>(p) * p.G;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float *dst = &sm.o[ln.w][ln.r][(4 * ln.grp + i) * (D / 16)];
-#pragma unroll
-            for (int b = 0; b < D / 16; b += 4)
-                *reinterpret_cast<f32x4 *>(dst + b) =
-                    f32x4{st.o[b][i], st.o[b + 1][i], st.o[b + 2][i], st.o[b + 3][i]};
-        }
-    }
-    __syncthreads();
-    for (int e = 4 * threadIdx.x; e < G * D; e += 4 * kDecodeThreads) {
-        const int g = e / D, d = e % D;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][g]);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        float wsum = 0.f;
-        if (M != kNegInf) {
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float c = __builtin_amdgcn_exp2f(sm.m[w][g] - M);
-                wsum += c * sm.l[w][g];
-                acc += c * *reinterpret_cast<const f32x4 *>(&sm.o[w][g][d]);
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int c0 = 16 * cb;
+        if (c0 + ln.r < RG) {
+            if (ln.grp == 0) {
+                sm.m[ln.w][ln.r] = st.m[cb];
+                sm.l[ln.w][ln.r] = st.l[cb];
             }
-            acc = acc * (1.0f / wsum);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float *dst = &sm.o[ln.w][ln.r][(4 * ln.grp + i) * (D / 16)];
+#pragma unroll
+                for (int b = 0; b < D / 16; b += 4)
+                    *reinterpret_cast<f32x4 *>(dst + b) = f32x4{
+                        st.o[cb][b][i], st.o[cb][b + 1][i], st.o[cb][b + 2][i], st.o[cb][b + 3][i]};
+            }
         }
-        *reinterpret_cast<f32x4 *>(p.part_o + (slot * G + g) * D + d) = acc;
-        if (d == 0)
-            p.part_lse[slot * G + g] =
-                M == kNegInf ? kNegInf : (M + log2f(wsum)) * kLn2;
+        __syncthreads();
+        const int n = min(16, RG - c0);
+        for (int e = 4 * threadIdx.x; e < n * D; e += 4 * kDecodeThreads) {
+            const int g = e / D, d = e % D;
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][g]);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            float wsum = 0.f;
+            if (M != kNegInf) {
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    const float c = __builtin_amdgcn_exp2f(sm.m[w][g] - M);
+                    wsum += c * sm.l[w][g];
+                    acc += c * *reinterpret_cast<const f32x4 *>(&sm.o[w][g][d]);
+                }
+                acc = acc * (1.0f / wsum);
+            }
+            const int64_t row = slot * RG + c0 + g;
+            *reinterpret_cast<f32x4 *>(p.part_o + row * D + d) = acc;
+            if (d == 0) p.part_lse[row] = M == kNegInf ? kNegInf : (M + log2f(wsum)) * kLn2;
+        }
+        if (cb + 1 < NCB) __syncthreads();   // the next block reuses sm.o
     }
     between();   // e.g. stage the next descriptor's Q: no wave reads it now
     __syncthreads();
@@ -435,10 +570,12 @@ __device__ __forceinline__ bool advance(const MapSource &src, int d_end, const P
     return same || next;
 }
 
-// Page id and live-token count of the tile at x; a tile outside the page
-// table or with a page id outside the pool reads page 0 and counts no token.
+// Page id of the tile at x and the request's tokens from the tile's first
+// on (nv, not clamped to 64: a query row that sees lag fewer tokens than the
+// request holds needs nv - lag); a tile outside the page table or with a
+// page id outside the pool reads page 0 and counts no token.
 __device__ __forceinline__ int locate(const DecodeParams &p, const Pos &x, int &nv) {
-    nv = min(kTile, x.L - kTile * x.t);
+    nv = x.L - kTile * x.t;
     int page = x.t < p.max_pages ? uniform(p.page_table[(int64_t)x.b * p.max_pages + x.t]) : -1;
     if ((unsigned)page >= (unsigned)p.num_pages) {
         page = 0;
@@ -447,36 +584,60 @@ __device__ __forceinline__ int locate(const DecodeParams &p, const Pos &x, int &
     return page;
 }
 
-// fp8: the q_scale of head g = r of (x.b, x.h); 1 for bf16.
-template <class KV>
-__device__ __forceinline__ float q_scale_of(const DecodeParams &p, const Pos &x, const Lane &ln) {
-    if constexpr (KV::kScaled) {
-        const int g = ln.r < p.G ? ln.r : 0;
-        return p.q_scale[(int64_t)x.b * p.Hq + (int64_t)x.h * p.G + g];
-    } else {
-        return 1.f;
+// fp8: the q_scale of each of this lane's columns of (x.b, x.h); 1 for bf16.
+template <class KV, int NCB, bool MR>
+__device__ __forceinline__ void q_scale_of(const DecodeParams &p, const Pos &x,
+                                           const Cols<NCB> &cols, float (&qs)[NCB]) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        if constexpr (KV::kScaled)
+            qs[cb] = p.q_scale[(int64_t)x.b * rows_per_req<MR>(p) * p.Hq + (int64_t)x.h * p.G +
+                               cols.qoff[cb]];
+        else
+            qs[cb] = 1.f;
     }
+}
+
+template <int NCB, bool MR>
+__device__ __forceinline__ Cols<NCB> columns(const DecodeParams &p, const Lane &ln) {
+    Cols<NCB> c;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = 16 * cb + ln.r;
+        if constexpr (MR) {
+            const bool real = col < p.R * p.G;
+            const int row = real ? col / p.G : 0;
+            c.lag[cb] = real ? p.R - 1 - row : 0;
+            c.qoff[cb] = real ? row * p.Hq + col % p.G : 0;
+        } else {
+            c.lag[cb] = 0;
+            c.qoff[cb] = col < p.G ? col : 0;
+        }
+    }
+    return c;
 }
 
 // Drains a run of descriptors tile by tile: while tile i is computed, tile
 // i + 1 (across descriptor boundaries) is being loaded into the other
 // register buffer.  The run starts at `first` and ends with descriptor
 // d_end - 1; partials go to slot d (by_desc) or to slot_base.
-template <class KV, int D, int GR>
-__device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR> &sm,
+template <class KV, int D, int GR, int NCB, bool MR>
+__device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB> &sm,
                                       const MapSource &src, const Pos &first, int d_end,
                                       int64_t slot_base, bool by_desc) {
     using Tile = typename KV::Tile;
     const Lane ln;
-    State<D> st;
+    const Cols<NCB> cols = columns<NCB, MR>(p, ln);
+    State<D, NCB> st;
     Pos cur = first;
     int nv_cur;
 
-    // Q rows past G stay zero for the whole kernel.
-    for (int i = threadIdx.x; i < 16 * (D / 2 + 4); i += kDecodeThreads) sm.q[i] = 0u;
+    // Q rows past R G stay zero for the whole kernel.
+    for (int i = threadIdx.x; i < 16 * NCB * (D / 2 + 4); i += kDecodeThreads) sm.q[i] = 0u;
     __syncthreads();
-    stage_q<KV, D, GR>(p, sm, cur.b, cur.h);
-    float qs = q_scale_of<KV>(p, cur, ln);
+    stage_q<KV, D, GR, NCB, MR>(p, sm, cur.b, cur.h);
+    float qs[NCB];
+    q_scale_of<KV, NCB, MR>(p, cur, cols, qs);
     st.reset();
     Tile ta, tb;
     const int pg = locate(p, cur, nv_cur);
@@ -495,14 +656,15 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR> &sm
         const int pg_n = locate(p, far, nv_n);
         KV::load_tile(p, pg_n, far.h, ln, nxt);
 
-        attend_tile<KV, D>(p, sm.q, qs, now, nv_cur, st, ln);
+        attend_tile<KV, D, NCB, MR>(p, sm.q, qs, now, nv_cur, cols, st, ln);
 
         if (!more || n.d != cur.d) {
-            merge_write<D, GR>(p, st, sm, by_desc ? (int64_t)cur.d : slot_base, ln, [&] {
-                if (more) stage_q<KV, D, GR>(p, sm, n.b, n.h);
-            });
+            merge_write<D, GR, NCB, MR>(p, st, sm, by_desc ? (int64_t)cur.d : slot_base, ln,
+                                        [&] {
+                                            if (more) stage_q<KV, D, GR, NCB, MR>(p, sm, n.b, n.h);
+                                        });
             if (!more) return false;
-            qs = q_scale_of<KV>(p, n, ln);
+            q_scale_of<KV, NCB, MR>(p, n, cols, qs);
             st.reset();
         }
         cur = n;
@@ -515,24 +677,321 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR> &sm
     }
 }
 
+// ---------------------------------------------------------------------------
+// The shared-tile path, for 2 .. 4 column blocks (multi-row steps with
+// R G > 16).  Holding every column's O in every wave (the path above) would
+// need NCB x D/4 accumulator registers per lane.  Here a workgroup is NCB
+// waves, wave w owns column block w for all 64 tokens of a tile, and the
+// tile sits in LDS, read by every column block:
+//   * all threads copy the next tile from HBM into registers (16-byte
+//     nontemporal loads) while the waves compute the current one from LDS;
+//   * a barrier, the registers go to LDS (rows padded by 16 bytes, so that
+//     16 lanes reading 16 rows at one column hit distinct banks), a barrier;
+//   * S^T = K Q^T per 16-token block on v_mfma_f32_16x16x32_{bf16,fp8};
+//     O^T += V^T P^T over 32 tokens per v_mfma_f32_16x16x32_bf16 (the lane's
+//     tokens of two 16-token blocks form its 8 k-slots);
+//   * a wave has its columns' whole softmax state, so a descriptor's partial
+//     is written without a merge between waves.
+// ---------------------------------------------------------------------------
+
+template <class KV, int D>
+struct SharedLds {
+    static constexpr int kRow = KV::kRowBytes + 16;   // padded row
+    alignas(16) uint8_t kv[2 * kTile * kRow];   // K rows 0 .. 63, then V rows
+    alignas(16) float ks[kTile];   // fp8 k and v scales of the tile's tokens
+    alignas(16) float vs[kTile];
+    __device__ const uint8_t *k() const { return kv; }
+    __device__ const uint8_t *v() const { return kv + kTile * kRow; }
+};
+
+// The tile as 16-byte chunks: K rows (chunk j < NK), V rows, then for fp8
+// the k and v scales (16 chunks each).  Thread t of T moves chunks
+// t, t + T, ...
+template <class KV, int D, int NCB>
+struct Staged {
+    static constexpr int T = 64 * NCB;
+    static constexpr int NK = kTile * KV::kRowBytes / 16;
+    static constexpr int NT = 2 * NK + (KV::kScaled ? 32 : 0);
+    static constexpr int NCH = (NT + T - 1) / T;
+    u32x4 c[NCH];
+};
+
+template <class KV, int D, int NCB>
+__device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int h,
+                                           Staged<KV, D, NCB> &st) {
+    using S = Staged<KV, D, NCB>;
+    const char *kb = tile_base(p.k, page, h, p.Hkv, KV::kRowBytes);
+    const char *vb = tile_base(p.v, page, h, p.Hkv, KV::kRowBytes);
+#pragma unroll
+    for (int i = 0; i < S::NCH; ++i) {
+        const int j = threadIdx.x + S::T * i;
+        if (S::T * (i + 1) <= S::NK) {   // all K (a whole round of chunks)
+            st.c[i] = ldg_stream<u32x4>(kb, 16 * j);
+        } else if (S::T * i >= S::NK && S::T * (i + 1) <= 2 * S::NK) {   // all V
+            st.c[i] = ldg_stream<u32x4>(vb, 16 * (j - S::NK));
+        } else if (j < S::NT) {
+            const char *src;
+            if (j < S::NK)
+                src = kb + 16 * j;
+            else if (j < 2 * S::NK)
+                src = vb + 16 * (j - S::NK);
+            else
+                src = tile_base(j < 2 * S::NK + 16 ? p.k_scale : p.v_scale, page, h, p.Hkv, 4) +
+                      16 * ((j - 2 * S::NK) & 15);
+            st.c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+        }
+    }
+}
+
+// K and V chunks go to row j / CPR, column j % CPR of the K-then-V rows
+// (CPR chunks per row); a round of T threads covers T / CPR whole rows, so
+// the address of round i is the thread's first address plus a constant.
+template <class KV, int D, int NCB>
+__device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, NCB> &st) {
+    using S = Staged<KV, D, NCB>;
+    constexpr int kRow = SharedLds<KV, D>::kRow, CPR = KV::kRowBytes / 16;
+    static_assert(S::T % CPR == 0, "a round of chunks covers whole rows");
+    uint8_t *base = sm.kv + (threadIdx.x / CPR) * kRow + 16 * (threadIdx.x % CPR);
+#pragma unroll
+    for (int i = 0; i < S::NCH; ++i) {
+        const int j = threadIdx.x + S::T * i;
+        if (S::T * (i + 1) <= 2 * S::NK) {   // a whole round of K / V chunks
+            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
+        } else if (j < 2 * S::NK) {
+            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
+        } else if (j < S::NT) {
+            const int q = j - 2 * S::NK;
+            *reinterpret_cast<u32x4 *>((q < 16 ? sm.ks : sm.vs) + 4 * (q & 15)) = st.c[i];
+        }
+    }
+}
+
+// One tile from LDS for the 16 columns of this wave's block, in two halves
+// of 32 tokens (token blocks 2 th, 2 th + 1), each folded into the running
+// softmax state on its own.  nv as in attend_tile; lag and qs are this
+// lane's column's.
+template <class KV, int D>
+__device__ __forceinline__ void attend_shared(const DecodeParams &p, const SharedLds<KV, D> &sm,
+                                              const typename KV::Q &q, float qs, int nv, int lag,
+                                              State<D, 1> &st, const Lane &ln) {
+    constexpr int kRow = SharedLds<KV, D>::kRow;
+    constexpr int VW = D / 32, VH = VW > 1 ? VW / 2 : 1;
+    const bool masked = nv - (p.R - 1) < 2 * 32;   // some row sees < 64 tokens
+    const int lim = nv - lag;
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+        f32x4 s[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {   // 16-token blocks tb = 2 th + u
+            const int tb = 2 * th + u;
+            u32x4 kc[KV::KC];
+            const uint8_t *row = sm.k() + (16 * tb + ln.r) * kRow + 16 * ln.grp;
+#pragma unroll
+            for (int i = 0; i < KV::KC; ++i) kc[i] = *reinterpret_cast<const u32x4 *>(row + 64 * i);
+            s[u] = KV::qk(kc, q);
+            if constexpr (KV::kScaled)
+                s[u] = s[u] * *reinterpret_cast<const f32x4 *>(sm.ks + 16 * tb + 4 * ln.grp) *
+                       (qs * p.scale_log2);
+            else
+                s[u] = s[u] * p.scale_log2;
+            if (masked) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * tb + 4 * ln.grp + i >= lim) s[u][i] = kNegInf;
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (__any(mx > st.m[0] + kSlack)) {   // stale reference max, as in attend_tile
+            const bool moves = mx > st.m[0] + kSlack;
+            const float m_new = moves ? mx : st.m[0];
+            const float alpha = moves ? __builtin_amdgcn_exp2f(st.m[0] - m_new) : 1.f;
+            st.l[0] *= alpha;
+#pragma unroll
+            for (int b = 0; b < D / 16; ++b) st.o[0][b] = st.o[0][b] * alpha;
+            st.m[0] = m_new;
+        }
+        const float m_use = st.m[0] == kNegInf ? 0.f : st.m[0];
+        float ps = 0.f;
+        uint32_t pw[4];   // P of tokens 32 th + 16 u + 4 grp + i, bf16 pairs
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 pr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(s[u][i] - m_use);
+            ps += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            if constexpr (KV::kScaled)
+                pr = pr * *reinterpret_cast<const f32x4 *>(sm.vs + 32 * th + 16 * u + 4 * ln.grp);
+            pw[2 * u] = pack_bf16(pr[0], pr[1]);
+            pw[2 * u + 1] = pack_bf16(pr[2], pr[3]);
+        }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        st.l[0] += ps;
+
+        // O^T += V^T P^T over the half's 32 tokens: k-slot e < 4 is token
+        // 32 th + 4 grp + e, e >= 4 token 32 th + 16 + 4 grp + e - 4.  V is
+        // read in halves of the lane's d-range (VH dwords of each token).
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+        for (int c0 = 0; c0 < VW; c0 += VH) {
+            uint32_t vv[8][VH];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tok = 32 * th + 16 * (j >> 2) + 4 * ln.grp + (j & 3);
+                KV::template v_part<VH>(sm.v() + tok * kRow, ln, c0, vv[j]);
+                if (nv < kTile && tok >= nv) {   // dead slots may hold NaN; P is 0 there
+#pragma unroll
+                    for (int c = 0; c < VH; ++c) vv[j][c] = 0u;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < VH; ++c) {
+                const u32x4 lo = {halves<false>(vv[0][c], vv[1][c]), halves<false>(vv[2][c], vv[3][c]),
+                                  halves<false>(vv[4][c], vv[5][c]), halves<false>(vv[6][c], vv[7][c])};
+                const u32x4 hi = {halves<true>(vv[0][c], vv[1][c]), halves<true>(vv[2][c], vv[3][c]),
+                                  halves<true>(vv[4][c], vv[5][c]), halves<true>(vv[6][c], vv[7][c])};
+                const int blk = 2 * (c0 + c);
+                st.o[0][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, lo), pb, st.o[0][blk], 0, 0, 0);
+                st.o[0][blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, hi), pb, st.o[0][blk + 1], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Normalise and write this wave's columns of partial slot `slot`.
+// The slot's rows start at a uniform address; the lane adds a 32-bit offset.
+template <int D>
+__device__ __forceinline__ void write_columns(const DecodeParams &p, const State<D, 1> &st,
+                                              int col0, int64_t slot, const Lane &ln) {
+    const int RG = p.R * p.G;
+    const int col = col0 + ln.r;
+    if (col >= RG) return;
+    const bool live = st.l[0] > 0.f;
+    const float inv = live ? 1.0f / st.l[0] : 0.f;
+    char *obase = reinterpret_cast<char *>(p.part_o + slot * RG * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)(col * D + (4 * ln.grp + i) * (D / 16)) * 4u;
+#pragma unroll
+        for (int b = 0; b < D / 16; b += 4)
+            *reinterpret_cast<f32x4 *>(obase + off + 4 * b) =
+                f32x4{st.o[0][b][i], st.o[0][b + 1][i], st.o[0][b + 2][i], st.o[0][b + 3][i]} *
+                inv;
+    }
+    if (ln.grp == 0)
+        p.part_lse[slot * RG + col] = live ? (st.m[0] + log2f(st.l[0])) * kLn2 : kNegInf;
+}
+
+// This lane's column of the shared-tile path: its query row's lag, its
+// q_scale offset and its Q row's offset in q (columns past R G read none).
+struct SharedCol {
+    bool real;
+    int lag, qoff;
+    __device__ SharedCol(const DecodeParams &p, const Lane &ln) {
+        const int col = 16 * ln.w + ln.r;
+        real = col < p.R * p.G;
+        const int qrow = real ? col / p.G : 0;
+        lag = real ? p.R - 1 - qrow : 0;
+        qoff = real ? qrow * p.Hq + col % p.G : 0;
+    }
+};
+
+// The lane's Q operand of (x.b, x.h), straight from q: the same d-ranges as
+// the K chunks (chunk i at byte 64 i + 16 grp of the row); zero for columns
+// past R G.
+template <class KV>
+__device__ __forceinline__ void load_q_direct(const DecodeParams &p, const Pos &x,
+                                              const SharedCol &c, const Lane &ln,
+                                              typename KV::Q &q) {
+    const char *base = reinterpret_cast<const char *>(p.q) +
+                       ((int64_t)x.b * p.R * p.Hq + (int64_t)x.h * p.G) * KV::kQRowBytes;
+    const uint32_t off = (uint32_t)(c.qoff * KV::kQRowBytes + 16 * ln.grp);
+#pragma unroll
+    for (int i = 0; i < KV::kQRowBytes / 64; ++i)
+        q.q[i] = c.real ? ldg<u32x4>(base, off + 64 * i) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// The drain loop of the shared-tile path (same descriptor walk as drain):
+// tile t + 1 is issued into registers before tile t is computed from LDS
+// and stored to LDS after it.
+template <class KV, int D, int NCB>
+__device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV, D> &sm,
+                                             const MapSource &src, const Pos &first, int d_end,
+                                             int64_t slot_base, bool by_desc) {
+    const Lane ln;
+    const SharedCol col(p, ln);
+    auto q_scale_at = [&](const Pos &x) __attribute__((always_inline)) -> float {
+        if constexpr (KV::kScaled)
+            return ldg<float>(p.q_scale + ((int64_t)x.b * p.R * p.Hq + (int64_t)x.h * p.G),
+                              (uint32_t)col.qoff * 4u);
+        else
+            return 1.f;
+    };
+
+    State<D, 1> st;
+    typename KV::Q q;
+    Pos cur = first;
+    int nv_cur;
+    Staged<KV, D, NCB> stg;
+    stage_load<KV, D, NCB>(p, locate(p, cur, nv_cur), cur.h, stg);
+    load_q_direct<KV>(p, cur, col, ln, q);
+    float qs = q_scale_at(cur);
+    st.reset();
+    stage_store<KV, D, NCB>(sm, stg);
+    __syncthreads();
+
+    while (true) {
+        Pos n;
+        const bool more = advance(src, d_end, cur, n);
+        const Pos far = pick(more, n, cur);
+        int nv_n;
+        stage_load<KV, D, NCB>(p, locate(p, far, nv_n), far.h, stg);
+
+        attend_shared<KV, D>(p, sm, q, qs, nv_cur, col.lag, st, ln);
+        __syncthreads();   // every wave is done with the tile in LDS
+
+        if (!more || n.d != cur.d) {
+            write_columns<D>(p, st, 16 * ln.w, by_desc ? (int64_t)cur.d : slot_base, ln);
+            if (!more) return;
+            load_q_direct<KV>(p, n, col, ln, q);
+            qs = q_scale_at(n);
+            st.reset();
+        }
+        stage_store<KV, D, NCB>(sm, stg);
+        __syncthreads();   // tile t + 1 is in LDS
+        cur = n;
+        nv_cur = nv_n;
+    }
+}
+
 // Three workgroups per CU (12 waves) keep enough KV loads in flight; the
-// kernel is written to fit the 168 registers per lane that allows.
-template <class KV, int D, int GR>
-__global__ void __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// one-block kernel is written to fit the 168 registers per lane that allows.
+// More column blocks hold more accumulators and run at two per CU.
+template <int NCB>
+constexpr int kDecodeWavesPerEu = NCB == 1 ? 3 : 2;
+
+template <class KV, int D, int GR, int NCB, bool MR>
+__global__ void __launch_bounds__(kDecodeThreads)
+__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<NCB>)))
 decode_kernel(DecodeParams p) {
-    __shared__ MergeLds<D, GR> sm;
+    __shared__ MergeLds<D, GR, NCB> sm;
     const MapLayout lay(p.B, p.Hkv, p.P);
     const int32_t *bin_off = p.map + lay.bin_off;
     const int d0 = uniform(bin_off[blockIdx.x]), d1 = uniform(bin_off[blockIdx.x + 1]);
     if (d0 >= d1) return;
     const MapSource src{p.map + lay.desc, p.map + lay.lens};
-    drain<KV, D, GR>(p, sm, src, src.read(d0), d1, 0, true);
+    drain<KV, D, GR, NCB, MR>(p, sm, src, src.read(d0), d1, 0, true);
 }
 
-template <class KV, int D, int GR>
+template <class KV, int D, int GR, int NCB, bool MR>
 __global__ void __launch_bounds__(kDecodeThreads)
 static_decode_kernel(DecodeParams p) {
-    __shared__ MergeLds<D, GR> sm;
+    __shared__ MergeLds<D, GR, NCB> sm;
     const int64_t slot = blockIdx.x;
     const int64_t seg = slot / p.splits;
     const int k = (int)(slot % p.splits);
@@ -549,33 +1008,108 @@ static_decode_kernel(DecodeParams p) {
         t1 = min<int64_t>(n, (k + 1) * ct);
     }
     if (t0 >= t1) {   // an empty split: no weight in the combine
-        if (threadIdx.x < p.G) p.part_lse[slot * p.G + threadIdx.x] = kNegInf;
+        const int RG = rows_per_req<MR>(p) * p.G;
+        if ((int)threadIdx.x < RG) p.part_lse[slot * RG + threadIdx.x] = kNegInf;
         return;
     }
     // The same drain as the dynamic kernel, over one range and no map: with
     // d_end = 1 and the range numbered 0 it never reads a descriptor.
-    drain<KV, D, GR>(p, sm, MapSource{nullptr, nullptr}, Pos{0, b, h, (int)t0, (int)t1, L}, 1,
-                     slot, false);
+    drain<KV, D, GR, NCB, MR>(p, sm, MapSource{nullptr, nullptr},
+                              Pos{0, b, h, (int)t0, (int)t1, L}, 1, slot, false);
 }
 
+// Shared-tile kernels (2 .. 4 column blocks): NCB waves per workgroup,
+// sized for three waves per SIMD.
+template <class KV, int D, int NCB>
+__global__ void __launch_bounds__(64 * NCB) __attribute__((amdgpu_waves_per_eu(3)))
+decode_shared_kernel(DecodeParams p) {
+    __shared__ SharedLds<KV, D> sm;
+    const MapLayout lay(p.B, p.Hkv, p.P);
+    const int32_t *bin_off = p.map + lay.bin_off;
+    const int d0 = uniform(bin_off[blockIdx.x]), d1 = uniform(bin_off[blockIdx.x + 1]);
+    if (d0 >= d1) return;
+    const MapSource src{p.map + lay.desc, p.map + lay.lens};
+    drain_shared<KV, D, NCB>(p, sm, src, src.read(d0), d1, 0, true);
+}
+
+template <class KV, int D, int NCB>
+__global__ void __launch_bounds__(64 * NCB) static_decode_shared_kernel(DecodeParams p) {
+    __shared__ SharedLds<KV, D> sm;
+    const int64_t slot = blockIdx.x;
+    const int64_t seg = slot / p.splits;
+    const int k = (int)(slot % p.splits);
+    const int b = (int)(seg / p.Hkv), h = (int)(seg % p.Hkv);
+    const int L = max(p.seq_lens[b], 0);
+    const int64_t n = (L + kTile - 1) / kTile;
+    int64_t t0, t1;
+    if (p.policy == 0) {
+        t0 = k * n / p.splits;
+        t1 = (k + 1) * n / p.splits;
+    } else {
+        const int64_t ct = p.param / kTile;
+        t0 = min<int64_t>(n, k * ct);
+        t1 = min<int64_t>(n, (k + 1) * ct);
+    }
+    if (t0 >= t1) {   // an empty split: no weight in the combine
+        const int RG = p.R * p.G;
+        for (int i = threadIdx.x; i < RG; i += 64 * NCB) p.part_lse[slot * RG + i] = kNegInf;
+        return;
+    }
+    drain_shared<KV, D, NCB>(p, sm, MapSource{nullptr, nullptr},
+                             Pos{0, b, h, (int)t0, (int)t1, L}, 1, slot, false);
+}
+
+// Column blocks of a workgroup: ceil(R G / 16), 1 .. 4.
+int column_blocks(int rows) { return (rows + 15) / 16; }
+
+// Waves of the shared-tile workgroup for NCB column blocks.  bf16 rows of
+// D = 128 at three waves would stage 11 chunks (44 registers) per thread,
+// beyond the 168 registers of three waves per SIMD; the spill waits for
+// every load each tile.  That case runs four waves, the fourth block padding.
+template <class KV, int D>
+constexpr int shared_waves(int ncb) {
+    return (ncb == 3 && !KV::kScaled && D == 128) ? 4 : ncb;
+}
+
+template <class KV, int D, int NCB>
+hipError_t launch_shared(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
+    if (dynamic)
+        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((static_decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB),
+                           0, stream, p);
+    return hipGetLastError();
+}
+
+template <class KV, int D, int GR, int NCB, bool MR>
+hipError_t launch_one(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
+    if (dynamic)
+        hipLaunchKernelGGL((decode_kernel<KV, D, GR, NCB, MR>), dim3(grid), dim3(kDecodeThreads),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL((static_decode_kernel<KV, D, GR, NCB, MR>), dim3(grid),
+                           dim3(kDecodeThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+// The instance for R G query rows: one 16-column block (8-row merge buffer
+// up to 8 rows), specialised for R = 1, or the shared-tile path for 2 .. 4
+// blocks.
 template <template <int> class KV, int D>
 hipError_t launch_for(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
-    if (p.G <= 8) {
-        if (dynamic)
-            hipLaunchKernelGGL((decode_kernel<KV<D>, D, 8>), dim3(grid), dim3(kDecodeThreads), 0,
-                               stream, p);
-        else
-            hipLaunchKernelGGL((static_decode_kernel<KV<D>, D, 8>), dim3(grid),
-                               dim3(kDecodeThreads), 0, stream, p);
-    } else {
-        if (dynamic)
-            hipLaunchKernelGGL((decode_kernel<KV<D>, D, 16>), dim3(grid), dim3(kDecodeThreads),
-                               0, stream, p);
-        else
-            hipLaunchKernelGGL((static_decode_kernel<KV<D>, D, 16>), dim3(grid),
-                               dim3(kDecodeThreads), 0, stream, p);
+    const int rows = p.R * p.G;
+    switch (column_blocks(rows)) {
+    case 1:
+        if (p.R == 1)
+            return rows <= 8 ? launch_one<KV<D>, D, 8, 1, false>(p, stream, dynamic, grid)
+                             : launch_one<KV<D>, D, 16, 1, false>(p, stream, dynamic, grid);
+        return rows <= 8 ? launch_one<KV<D>, D, 8, 1, true>(p, stream, dynamic, grid)
+                         : launch_one<KV<D>, D, 16, 1, true>(p, stream, dynamic, grid);
+    case 2: return launch_shared<KV<D>, D, 2>(p, stream, dynamic, grid);
+    case 3: return launch_shared<KV<D>, D, shared_waves<KV<D>, D>(3)>(p, stream, dynamic, grid);
+    default: return launch_shared<KV<D>, D, 4>(p, stream, dynamic, grid);
     }
-    return hipGetLastError();
 }
 
 hipError_t dispatch(const DecodeParams &p, int head_dim, int kv_dtype, hipStream_t stream,
@@ -588,23 +1122,33 @@ hipError_t dispatch(const DecodeParams &p, int head_dim, int kv_dtype, hipStream
                            : launch_for<Fp8, 64>(p, stream, dynamic, grid);
 }
 
+// The dynamic kernel launch_for picks for `rows` rows with R = 1 when
+// rows <= 16 (the resident count does not depend on R otherwise).
+template <template <int> class KV, int D>
+const void *decode_fn(int rows, int &threads) {
+    const int ncb = column_blocks(rows);
+    threads = ncb == 1 ? kDecodeThreads : 64 * shared_waves<KV<D>, D>(ncb);
+    switch (column_blocks(rows)) {
+    case 1:
+        return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false>
+                         : (const void *)decode_kernel<KV<D>, D, 16, 1, false>;
+    case 2: return (const void *)decode_shared_kernel<KV<D>, D, 2>;
+    case 3: return (const void *)decode_shared_kernel<KV<D>, D, shared_waves<KV<D>, D>(3)>;
+    default: return (const void *)decode_shared_kernel<KV<D>, D, 4>;
+    }
+}
+
 }  // namespace
 
-int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t group) {
+int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t rows) {
     int n = 0;
-    const void *fn;
-    const bool small = group <= 8;
-    if (kv_dtype == HPCATTN_KV_BF16)
-        fn = head_dim == 128 ? (small ? (const void *)decode_kernel<Bf16<128>, 128, 8>
-                                      : (const void *)decode_kernel<Bf16<128>, 128, 16>)
-                             : (small ? (const void *)decode_kernel<Bf16<64>, 64, 8>
-                                      : (const void *)decode_kernel<Bf16<64>, 64, 16>);
-    else
-        fn = head_dim == 128 ? (small ? (const void *)decode_kernel<Fp8<128>, 128, 8>
-                                      : (const void *)decode_kernel<Fp8<128>, 128, 16>)
-                             : (small ? (const void *)decode_kernel<Fp8<64>, 64, 8>
-                                      : (const void *)decode_kernel<Fp8<64>, 64, 16>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kDecodeThreads, 0) != hipSuccess)
+    int threads = 0;
+    const void *fn = kv_dtype == HPCATTN_KV_BF16
+                         ? (head_dim == 128 ? decode_fn<Bf16, 128>(rows, threads)
+                                            : decode_fn<Bf16, 64>(rows, threads))
+                         : (head_dim == 128 ? decode_fn<Fp8, 128>(rows, threads)
+                                            : decode_fn<Fp8, 64>(rows, threads));
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess)
         return 0;
     return n;
 }

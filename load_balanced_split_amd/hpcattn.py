@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PAGE_SIZE = 64
 MAX_BATCH = 8192
 MAX_GROUP = 16
+MAX_ROWS = 64
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
 
@@ -41,6 +42,7 @@ class hpcattn_dims(ctypes.Structure):
         ("num_pages", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
+        ("q_rows", ctypes.c_int32),
     ]
 
 
@@ -136,11 +138,12 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_dims(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_req, num_pages,
-              kv_dtype=KV_BF16, sm_scale=None) -> hpcattn_dims:
+              kv_dtype=KV_BF16, sm_scale=None, q_rows=1) -> hpcattn_dims:
+    """q_rows: query rows per request (1 for decode, 1 + drafts to verify)."""
     if sm_scale is None:
         sm_scale = head_dim ** -0.5
     return hpcattn_dims(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_req,
-                        num_pages, kv_dtype, sm_scale)
+                        num_pages, kv_dtype, sm_scale, q_rows)
 
 
 class TaskMap:
@@ -168,9 +171,10 @@ def hpcattn_static_max_partials(batch, num_kv_heads, policy, param, max_seq_len)
     return int(_lib.hpcattn_static_max_partials(batch, num_kv_heads, policy, param, max_seq_len))
 
 
-def hpcattn_suggest_num_bins(head_dim: int, kv_dtype: int, group: int) -> int:
-    """Co-resident decode workgroups on the current device (needs a GPU)."""
-    n = int(_lib.hpcattn_suggest_num_bins(head_dim, kv_dtype, group))
+def hpcattn_suggest_num_bins(head_dim: int, kv_dtype: int, rows: int) -> int:
+    """Co-resident decode workgroups on the current device for rows = q_rows * G
+    query rows per KV head (needs a GPU)."""
+    n = int(_lib.hpcattn_suggest_num_bins(head_dim, kv_dtype, rows))
     _check(min(n, 0), "hpcattn_suggest_num_bins")
     return n
 

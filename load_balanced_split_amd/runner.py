@@ -24,25 +24,28 @@ class DecodeRunner:
         B = prob.seq_lens.shape[0]
         self.B, self.Hq, self.Hkv, self.D = B, w.num_q_heads, w.num_kv_heads, w.head_dim
         self.G = self.Hq // self.Hkv
+        self.R = w.q_rows
+        self.rows = self.R * self.G          # query rows per KV head
         self.fp8 = w.kv_dtype == "fp8"
         if num_bins is None:
             num_bins = w.num_bins
         if num_bins is None:
             num_bins = H.hpcattn_suggest_num_bins(self.D, H.KV_FP8_E4M3 if self.fp8 else H.KV_BF16,
-                                                  self.G)
+                                                  self.rows)
         self.num_bins = num_bins
         self.min_tiles = w.min_tiles if min_tiles is None else min_tiles
         self.dims = H.make_dims(B, self.Hq, self.Hkv, self.D, prob.page_table.shape[1],
                                 prob.num_pages, H.KV_FP8_E4M3 if self.fp8 else H.KV_BF16,
-                                prob.sm_scale)
+                                prob.sm_scale, self.R)
         self.seq_lens = torch.from_numpy(prob.seq_lens.astype(np.int32)).to(device)
         self.page_table = torch.from_numpy(prob.page_table).to(device)
         self.task_map = H.alloc_task_map(B, self.Hkv, self.num_bins, device)
         rows = H.hpcattn_max_partials(B, self.Hkv, self.num_bins)
-        self.part_o = torch.empty((rows, self.G, self.D), dtype=torch.float32, device=device)
-        self.part_lse = torch.empty((rows, self.G), dtype=torch.float32, device=device)
-        self.out = torch.empty((B, self.Hq, self.D), dtype=torch.bfloat16, device=device)
-        self.out_lse = torch.empty((B, self.Hq), dtype=torch.float32, device=device)
+        self.part_o = torch.empty((rows, self.rows, self.D), dtype=torch.float32, device=device)
+        self.part_lse = torch.empty((rows, self.rows), dtype=torch.float32, device=device)
+        lead = w.q_shape(B)[:-1]
+        self.out = torch.empty(lead + (self.D,), dtype=torch.bfloat16, device=device)
+        self.out_lse = torch.empty(lead, dtype=torch.float32, device=device)
         self._static = {}
 
     def _kv(self, layer: int):
@@ -81,8 +84,8 @@ class DecodeRunner:
             if rows <= 0:
                 raise ValueError("bad static policy %r" % (key,))
             self._static[key] = (
-                torch.empty((rows, self.G, self.D), dtype=torch.float32, device=self.device),
-                torch.empty((rows, self.G), dtype=torch.float32, device=self.device),
+                torch.empty((rows, self.rows, self.D), dtype=torch.float32, device=self.device),
+                torch.empty((rows, self.rows), dtype=torch.float32, device=self.device),
                 max_len)
         return self._static[key]
 

@@ -69,10 +69,17 @@ class Workload:
     num_bins: Optional[int] = None  # persistent workgroups (one bin each); None: as many
                                     # as the device holds at once
     min_tiles: int = 32      # minimum-work floor, tiles per bin
+    q_rows: int = 1          # query rows per request: 1 + draft tokens to verify
 
     @property
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
+
+    def q_shape(self, batch: int):
+        """[B, H_q, D], or [B, R, H_q, D] with R = q_rows > 1."""
+        if self.q_rows == 1:
+            return (batch, self.num_q_heads, self.head_dim)
+        return (batch, self.q_rows, self.num_q_heads, self.head_dim)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -81,6 +88,10 @@ WORKLOADS: Dict[str, Workload] = {
     "mixed": Workload("mixed", _mixed, 8, 64, 128, "bf16", layers=32),
     "heavy_tail": Workload("heavy_tail", _heavy_tail, 8, 64, 128, "bf16"),
     "fp8": Workload("fp8", _fp8, 8, 64, 128, "fp8"),
+    # A draft-verify step ("SGLang Low-Latency Mode", section 1: the confirmed
+    # token and five drafts per request, six rows) over the mixed length mix.
+    "mtp": Workload("mtp", _mixed, 8, 64, 128, "bf16", layers=32, q_rows=6),
+    "mtp_fp8": Workload("mtp_fp8", _fp8, 8, 64, 128, "fp8", q_rows=6),
 }
 
 
@@ -138,10 +149,10 @@ class Problem:
     seq_lens: np.ndarray
     page_table: np.ndarray
     num_pages: int
-    q: torch.Tensor                          # bf16 [B,Hq,D] or uint8
+    q: torch.Tensor                          # bf16 [B,Hq,D] ([B,R,Hq,D]) or uint8
     k_pages: list                            # per layer [num_pages,Hkv,64,D]
     v_pages: list
-    q_scale: Optional[torch.Tensor] = None   # fp32 [B,Hq]
+    q_scale: Optional[torch.Tensor] = None   # fp32 [B,Hq] ([B,R,Hq])
     k_scale: Optional[list] = None           # per layer fp32 [num_pages,Hkv,64]
     v_scale: Optional[list] = None
     sm_scale: float = 1.0
@@ -162,8 +173,9 @@ def make_problem(name: str, seed: int = 0, device="cpu", layers: Optional[int] =
     B, Hq, Hkv, D = L.shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim
     pool_shape = (num_pages, Hkv, PAGE, D)
     sm_scale = 1.0 / math.sqrt(D)
+    qshape = w.q_shape(B)
     if w.kv_dtype == "bf16":
-        q = (torch.randn((B, Hq, D), generator=gen, device=device) * q_mult).to(torch.bfloat16)
+        q = (torch.randn(qshape, generator=gen, device=device) * q_mult).to(torch.bfloat16)
         ks, vs = [], []
         for _ in range(nl):
             k = randn_bf16(pool_shape, gen, device)
@@ -176,7 +188,7 @@ def make_problem(name: str, seed: int = 0, device="cpu", layers: Optional[int] =
             vs.append(v)
         return Problem(w, L, pt, num_pages, q.contiguous(), ks, vs, sm_scale=sm_scale)
     if w.kv_dtype == "fp8":
-        qf = torch.randn((B, Hq, D), generator=gen, device=device) * q_mult
+        qf = torch.randn(qshape, generator=gen, device=device) * q_mult
         q, q_scale = quantize_e4m3(qf)
         ks, vs, kss, vss = [], [], [], []
         for _ in range(nl):

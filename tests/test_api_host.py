@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(H):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(H.EXPORTS)
-    assert H.hpcattn_version() == 100
+    assert H.hpcattn_version() == 200
 
 
 def test_size_queries_match_layout(H):
@@ -79,7 +79,7 @@ def test_plan_rejects_bad_arguments(H):
 
 def _dims(H, **kw):
     d = dict(batch=4, num_q_heads=4, num_kv_heads=1, head_dim=64, max_pages_per_req=16,
-             num_pages=22, kv_dtype=H.KV_BF16, sm_scale=0.125)
+             num_pages=22, kv_dtype=H.KV_BF16, sm_scale=0.125, q_rows=1)
     d.update(kw)
     return H.hpcattn_dims(**d)
 
@@ -108,6 +108,9 @@ def test_decode_rejects_bad_arguments(H):
     assert _decode(H, _dims(H, kv_dtype=H.KV_FP8_E4M3), m, q_scale=FAKE,
                    k_scale=FAKE) == H.ERR_DTYPE                    # fp8 missing v_scale
     assert _decode(H, _dims(H, sm_scale=float("nan")), m) == H.ERR_ARG
+    assert _decode(H, _dims(H, q_rows=0), m) == H.ERR_SHAPE       # at least one row
+    assert _decode(H, _dims(H, q_rows=17), m) == H.ERR_SHAPE      # R G = 68 > 64 rows
+    assert _decode(H, _dims(H, num_q_heads=16, q_rows=5), m) == H.ERR_SHAPE   # 80 rows
     assert _decode(H, _dims(H), m, rows=4 * 1 + 8 - 2) == H.ERR_WORKSPACE
     small = _map(H, nbytes=16)
     assert _decode(H, _dims(H), small) == H.ERR_WORKSPACE
@@ -140,7 +143,7 @@ def test_suggest_and_probe_reject_bad_arguments(H):
     lib = H._lib
     assert lib.hpcattn_suggest_num_bins(96, H.KV_BF16, 8) == H.ERR_ARG
     assert lib.hpcattn_suggest_num_bins(128, 5, 8) == H.ERR_ARG
-    assert lib.hpcattn_suggest_num_bins(128, H.KV_BF16, 17) == H.ERR_ARG
+    assert lib.hpcattn_suggest_num_bins(128, H.KV_BF16, 65) == H.ERR_ARG
     assert lib.hpcattn_probe_stream_read(None, 1024, 8, 0, FAKE, None) == H.ERR_NULL
     assert lib.hpcattn_probe_stream_read(FAKE, 1000, 8, 0, FAKE, None) == H.ERR_ARG
     assert lib.hpcattn_probe_stream_read(FAKE, 1024, 0, 0, FAKE, None) == H.ERR_ARG
