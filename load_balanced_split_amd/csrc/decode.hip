@@ -466,12 +466,11 @@ __device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR, N
     constexpr int RW = KV::kQRowBytes / 4, QS = RW + 4;
     const int R = rows_per_req<MR>(p);
     for (int r = 0; r < R; ++r) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(
-            reinterpret_cast<const char *>(p.q) +
-            (((int64_t)b * R + r) * p.Hq + (int64_t)h * p.G) * KV::kQRowBytes);
+        const char *src = reinterpret_cast<const char *>(p.q) +
+                          (((int64_t)b * R + r) * p.Hq + (int64_t)h * p.G) * KV::kQRowBytes;
         uint32_t *dst = sm.q + r * p.G * QS;
         for (int i = threadIdx.x; i < p.G * RW; i += kDecodeThreads)
-            dst[(i / RW) * QS + i % RW] = src[i];
+            dst[(i / RW) * QS + i % RW] = ldg<uint32_t>(src, 4u * (uint32_t)i);
     }
 }
 
@@ -517,9 +516,12 @@ __device__ __forceinline__ void merge_write(const DecodeParams &p, State<D, NCB>
                 }
                 acc = acc * (1.0f / wsum);
             }
-            const int64_t row = slot * RG + c0 + g;
-            *reinterpret_cast<f32x4 *>(p.part_o + row * D + d) = acc;
-            if (d == 0) p.part_lse[row] = M == kNegInf ? kNegInf : (M + log2f(wsum)) * kLn2;
+            // the slot's rows start at a uniform address, plus a 32-bit offset
+            char *obase = reinterpret_cast<char *>(p.part_o + slot * RG * D);
+            *reinterpret_cast<f32x4 *>(obase + 4u * (uint32_t)((c0 + g) * D + d)) = acc;
+            if (d == 0)
+                p.part_lse[slot * RG + c0 + g] =
+                    M == kNegInf ? kNegInf : (M + log2f(wsum)) * kLn2;
         }
         if (cb + 1 < NCB) __syncthreads();   // the next block reuses sm.o
     }
@@ -540,6 +542,13 @@ struct Pos {
 // scalar register so tile bases use the scalar-base load form.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// A read-only int32 at a wave-uniform index, through the scalar memory path
+// (constant address space): its wait counts scalar loads only, so it never
+// waits for the KV tiles in flight on the vector memory path.
+__device__ __forceinline__ int sload(const int32_t *base, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t *)base)[i];
+}
+
 // Field-wise select (a whole-struct ?: would be lowered through memory).
 __device__ __forceinline__ Pos pick(bool c, const Pos &a, const Pos &b) {
     return Pos{c ? a.d : b.d, c ? a.b : b.b, c ? a.h : b.h,
@@ -551,9 +560,9 @@ struct MapSource {
     const int32_t *desc;
     const int32_t *lens;
     __device__ __forceinline__ Pos read(int d) const {
-        const int32_t *q = desc + 4 * (int64_t)d;
-        const int b = uniform(q[0]);
-        return Pos{d, b, uniform(q[1]), uniform(q[2]), uniform(q[3]), uniform(lens[b])};
+        const int64_t o = 4 * (int64_t)d;
+        const int b = sload(desc, o);
+        return Pos{d, b, sload(desc, o + 1), sload(desc, o + 2), sload(desc, o + 3), sload(lens, b)};
     }
 };
 
@@ -576,7 +585,7 @@ __device__ __forceinline__ bool advance(const MapSource &src, int d_end, const P
 // page id outside the pool reads page 0 and counts no token.
 __device__ __forceinline__ int locate(const DecodeParams &p, const Pos &x, int &nv) {
     nv = x.L - kTile * x.t;
-    int page = x.t < p.max_pages ? uniform(p.page_table[(int64_t)x.b * p.max_pages + x.t]) : -1;
+    int page = x.t < p.max_pages ? sload(p.page_table, (int64_t)x.b * p.max_pages + x.t) : -1;
     if ((unsigned)page >= (unsigned)p.num_pages) {
         page = 0;
         nv = 0;
