@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn µs/step + KV-read GB/s (% HBM peak), mixed-length GQA batch"
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_mixed_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "load_balanced_split_amd", "csrc", "decode.hip")
 
 DESCRIPTIONS = {
@@ -275,12 +275,13 @@ def unfused_prologue_us(qkv, pos, slots, w, kp, vp, sc, Hq, Hkv, D, fp8, stream,
     return a.elapsed_time(b) / reps * 1e3
 
 
-def traffic_from_profile():
-    """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on the current decode source."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def traffic_from_profile(workload: str):
+    """HBM bytes per decode launch from the committed counter summary of this
+    workload, if there is one and it was taken on the current decode source."""
+    path = os.path.join(PROFILES, "decode_%s_traffic.md" % workload)
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_TRAFFIC).read()
+    text = open(path).read()
     m = re.search(r"decode_source_sha256:\s*([0-9a-f]{64})", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t:
@@ -470,8 +471,9 @@ def main():
                          "step_p90": round(sorted(step_ms)[int(0.9 * (len(step_ms) - 1))] * 1e3, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(),
-                     "kernel": "decode_kernel (one launch = one layer's live KV)"},
+                     "traffic": traffic_from_profile(name),
+                     "kernel": "%s (one launch = one layer's live KV)" % (
+                         "decode_shared_kernel" if w.q_rows * w.group > 16 else "decode_kernel")},
         "wall_s_timed": round(wall, 3),
         "launch": "eager" if args.eager else "hip_graph (%d step(s) per replay)" % per_graph,
     }
