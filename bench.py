@@ -425,10 +425,31 @@ def main():
             step_ms.append(a.elapsed_time(b) / per_graph)
     wall = time.perf_counter() - wall0
 
+    # The same step with decode and combine fused into one launch per layer
+    # (hpcattn_decode_combine), replayed the same way.
+    def fused_step(k):
+        run.plan()
+        for layer in range(layers):
+            run.decode_combine((k * layers + layer) % pools)
+
+    gf = capture(lambda: [fused_step(k) for k in range(per_graph)])
+    gf.replay()
+    torch.cuda.synchronize()
+    fused_ms = []
+    for _ in range(max(1, args.steps // per_graph)):
+        a, b = events()
+        a.record(stream)
+        gf.replay()
+        b.record(stream)
+        b.synchronize()
+        fused_ms.append(a.elapsed_time(b) / per_graph)
+    med_fused = statistics.median(fused_ms)
+
     # Per-kernel GPU time, each kernel back to back in its own graph.
     n_dec = max(layers, pools) if multi_layer else pools
     dec_avg = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec)
     combine_ms = graph_avg_ms(lambda: [run.combine() for _ in range(16)], 16)
+    fused_avg = graph_avg_ms(lambda: [run.decode_combine(i % pools) for i in range(n_dec)], n_dec)
     plan_ms = graph_avg_ms(lambda: [run.plan() for _ in range(16)], 16)
     torch.cuda.synchronize()
 
@@ -474,6 +495,10 @@ def main():
                      "traffic": traffic_from_profile(name),
                      "kernel": "%s (one launch = one layer's live KV)" % (
                          "decode_shared_kernel" if w.q_rows * w.group > 16 else "decode_kernel")},
+        "fused": {"us_per_step": round(med_fused * 1e3, 1),
+                  "gbs": round(kv_bytes_layer * layers / (med_fused * 1e-3) / 1e9, 2),
+                  "decode_combine_avg_us": round(fused_avg * 1e3, 2),
+                  "speedup_vs_two_launches": round(med_step / med_fused, 4)},
         "wall_s_timed": round(wall, 3),
         "launch": "eager" if args.eager else "hip_graph (%d step(s) per replay)" % per_graph,
     }

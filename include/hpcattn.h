@@ -17,6 +17,7 @@
  *                       per descriptor.
  *   3. hpcattn_combine  per layer: merge each (request, KV head)'s partials
  *                       under the global softmax.
+ *   hpcattn_decode_combine does 2 and 3 in one launch.
  *   hpcattn_static_decode is the static split-KV scheme the pages compare
  *   against (fixed split count, or fixed chunk size), for ablation.
  *
@@ -178,9 +179,9 @@ int hpcattn_plan(const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads,
  * workgroup drains its bin, computing attention over one or more contiguous
  * KV tiles per descriptor and writing a partial output with its log-sum-exp).
  *
- * Launches map->num_bins workgroups of 256 threads; bin i is drained by
- * workgroup i.  Writes part_o / part_lse rows 0 .. num_desc - 1 and nothing
- * else.  dims->batch and dims->num_kv_heads must equal the map's.
+ * Launches map->num_bins workgroups (256 threads, or 64 per 16 query rows
+ * of a KV head when q_rows * G > 16); bin i is drained by workgroup i.
+ * Writes part_o / part_lse rows 0 .. num_desc - 1 and nothing else.  dims->batch and dims->num_kv_heads must equal the map's.
  * q_scale, k_scale, v_scale: NULL for bf16, required for fp8.
  * part_o / part_lse: at least hpcattn_max_partials(B, H_kv, P) rows;
  * part_o_rows gives the caller's row capacity.
@@ -207,6 +208,39 @@ int hpcattn_decode(const hpcattn_dims *dims, const void *q, const float *q_scale
 int hpcattn_combine(const hpcattn_dims *dims, const hpcattn_task_map *map,
                     const float *part_o, const float *part_lse, void *out,
                     float *out_lse, void *stream);
+
+/*
+ * Decode and combine in one launch: the same result as hpcattn_decode
+ * followed by hpcattn_combine, with one kernel per layer instead of two
+ * ("SGLang Low-Latency Mode: Kernels and Runtime", section 3: each small
+ * kernel costs its launch and its tail even under HIP graphs).
+ *
+ * A segment cut into one chunk writes its out rows directly.  Otherwise
+ * each workgroup that finishes a chunk writes its partial with the
+ * device-coherent cache policy and increments tickets[b * H_kv + h]; the
+ * workgroup that takes the last ticket merges the segment's partials as
+ * hpcattn_combine does (up to summation order) and resets the ticket to 0.
+ * No workgroup ever waits for another.  Where fusing does not pay -- a mean
+ * of 8 or more chunks per segment (S + P - 1 descriptors over S = B H_kv
+ * segments), or more than 16 query rows per KV head -- the call runs
+ * hpcattn_decode and hpcattn_combine instead, with the same result.
+ *
+ * tickets: device int32 [num_tickets >= B * H_kv], all zero on entry; the
+ *   call leaves them zero.  Zero them once after allocating; reuse freely
+ *   across layers and steps.  Calls that share a tickets buffer must not
+ *   overlap.
+ * part_o / part_lse: scratch for the multi-chunk segments, sized as for
+ *   hpcattn_decode.  out / out_lse: as for hpcattn_combine (out_lse may be
+ *   NULL).  Errors as for hpcattn_decode, plus NULL tickets / out and
+ *   num_tickets < B * H_kv (HPCATTN_ERR_WORKSPACE).
+ */
+int hpcattn_decode_combine(const hpcattn_dims *dims, const void *q, const float *q_scale,
+                           const void *k_pages, const void *v_pages,
+                           const float *k_scale, const float *v_scale,
+                           const int32_t *page_table, const hpcattn_task_map *map,
+                           float *part_o, float *part_lse, int64_t part_o_rows,
+                           int32_t *tickets, int64_t num_tickets, void *out,
+                           float *out_lse, void *stream);
 
 /*
  * Static split-KV decode, the scheme the dynamic one replaces ("Attention:

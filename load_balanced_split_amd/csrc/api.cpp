@@ -145,6 +145,44 @@ int hpcattn_decode(const hpcattn_dims *dims, const void *q, const float *q_scale
     return launch_status(launch_decode(p, dims->head_dim, dims->kv_dtype, (hipStream_t)stream));
 }
 
+int hpcattn_decode_combine(const hpcattn_dims *dims, const void *q, const float *q_scale,
+                           const void *k_pages, const void *v_pages, const float *k_scale,
+                           const float *v_scale, const int32_t *page_table,
+                           const hpcattn_task_map *map, float *part_o, float *part_lse,
+                           int64_t part_o_rows, int32_t *tickets, int64_t num_tickets, void *out,
+                           float *out_lse, void *stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    rc = check_operands(dims, q, q_scale, k_pages, v_pages, k_scale, v_scale, page_table);
+    if (rc) return rc;
+    rc = check_map(dims, map);
+    if (rc) return rc;
+    if (!part_o || !part_lse || !tickets || !out) return HPCATTN_ERR_NULL;
+    if (part_o_rows < hpcattn_max_partials(map->batch, map->num_kv_heads, map->num_bins) ||
+        num_tickets < (int64_t)map->batch * map->num_kv_heads)
+        return HPCATTN_ERR_WORKSPACE;
+    DecodeParams p = make_params(dims, q, q_scale, k_pages, v_pages, k_scale, v_scale,
+                                 page_table, part_o, part_lse);
+    p.map = map->words;
+    p.P = map->num_bins;
+    // Fuse where it pays (measured): segments of a few chunks on the per-wave
+    // kernel.  Long segments (a mean of >= 8 chunks: the last workgroup would
+    // merge many partials alone) and workgroups of more than 16 query rows run
+    // decode and combine as two launches, with the same result.
+    const int64_t S = (int64_t)map->batch * map->num_kv_heads;
+    const int64_t mean_chunks = (S + map->num_bins - 1 + S - 1) / S;
+    const int rows = dims->q_rows * (dims->num_q_heads / dims->num_kv_heads);
+    if (mean_chunks >= 8 || rows > 16) {
+        hipError_t e = launch_decode(p, dims->head_dim, dims->kv_dtype, (hipStream_t)stream);
+        if (e != hipSuccess) return HPCATTN_ERR_LAUNCH;
+        return hpcattn_combine(dims, map, part_o, part_lse, out, out_lse, stream);
+    }
+    p.out = out;
+    p.out_lse = out_lse;
+    p.tickets = tickets;
+    return launch_status(launch_decode(p, dims->head_dim, dims->kv_dtype, (hipStream_t)stream));
+}
+
 int hpcattn_combine(const hpcattn_dims *dims, const hpcattn_task_map *map,
                     const float *part_o, const float *part_lse, void *out, float *out_lse,
                     void *stream) {

@@ -46,6 +46,10 @@ struct DecodeParams {
     int32_t policy, param;  // static split policy and its parameter
     int32_t splits;         // static: slots per segment
     float scale_log2;       // sm_scale * log2(e)
+    // decode + combine in one launch (dynamic only; out == NULL: off)
+    void *out;              // bf16 [B, R, Hq, D]
+    float *out_lse;         // [B, R, Hq] or NULL
+    int32_t *tickets;       // [B * Hkv], zero on entry and on exit
 };
 
 struct CombineParams {

@@ -99,6 +99,17 @@ __device__ __forceinline__ const char *tile_base(const void *pool, int page, int
            ((int64_t)page * Hkv + h) * (int64_t)kTile * row_bytes;
 }
 
+// Wave-uniform by construction (same address for every lane): keep it in a
+// scalar register so tile bases use the scalar-base load form.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// A read-only int32 at a wave-uniform index, through the scalar memory path
+// (constant address space): its wait counts scalar loads only, so it never
+// waits for the KV tiles in flight on the vector memory path.
+__device__ __forceinline__ int sload(const int32_t *base, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t *)base)[i];
+}
+
 // ---------------------------------------------------------------------------
 // Element formats.  Each provides the per-lane register image of one tile's
 // share of K and V, of the descriptor's Q, and the two MFMA operand builders.
@@ -455,6 +466,7 @@ struct MergeLds {
     // padded by 4 dwords so that the per-tile operand reads are bank-conflict
     // free.
     uint32_t q[16 * NCB * (D / 2 + 4)];
+    int last;   // the fused combine: this workgroup merges the segment
 };
 
 // Copy the R G query rows of (b, h) into the LDS Q rows: LDS row r G + g is
@@ -474,13 +486,159 @@ __device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR, N
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode and combine in one launch ("Scheduling around live KV work": the
+// partials of a (request, KV head) segment are merged under the global
+// softmax once all of them exist).  A segment cut into one chunk writes its
+// output directly.  Otherwise every workgroup that finishes one of its
+// chunks publishes the partial (agent-scope release) and takes a ticket;
+// the one holding the last ticket merges the segment and resets the ticket.
+// Nothing waits for another workgroup.
+// ---------------------------------------------------------------------------
+
+// Output row of partial row c = r G + g of segment (b, h): out is
+// [B, R, H_q, D].
+__device__ __forceinline__ int64_t out_row(const DecodeParams &p, int b, int h, int c) {
+    return ((int64_t)b * p.R + c / p.G) * p.Hq + (int64_t)h * p.G + c % p.G;
+}
+
+__device__ __forceinline__ void store_bf16x4(void *out, int64_t elem, const f32x4 &v) {
+    const u32x2 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    *reinterpret_cast<u32x2 *>(reinterpret_cast<__bf16 *>(out) + elem) = w;
+}
+
+// Partials that another workgroup merges are written and read with the
+// device-coherent cache policy (sc1: the L2 of another XCD cannot hold a
+// stale copy), through buffer descriptors based at the rows concerned, so
+// that no release / acquire fence (a write-back or invalidate of the whole
+// L2 of an XCD) is needed around the ticket.  Out-of-range offsets read 0
+// and write nothing.
+constexpr int kCoherent = 16;          // cache policy: sc1
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const float *base, int64_t floats) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0,
+                                             (int)(floats * 4), kRawBufferWord3);
+}
+
+__device__ __forceinline__ void publish4(__amdgpu_buffer_rsrc_t r, uint32_t byte, const f32x4 &v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte, 0,
+                                           kCoherent);
+}
+
+__device__ __forceinline__ void publish(__amdgpu_buffer_rsrc_t r, uint32_t byte, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)byte, 0, kCoherent);
+}
+
+__device__ __forceinline__ f32x4 fetch4(__amdgpu_buffer_rsrc_t r, uint32_t byte) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte, 0,
+                                                                         kCoherent));
+}
+
+__device__ __forceinline__ float fetch(__amdgpu_buffer_rsrc_t r, uint32_t byte) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte, 0, kCoherent));
+}
+
+// Merge the n partials k0 .. k0 + n - 1 of segment (b, h) into out / out_lse
+// (all threads of the workgroup; lse is natural log, -inf for no weight).
+// One pass with a running maximum, kMergeUnroll chunks' loads in flight.
+constexpr int kMergeUnroll = 4;
+
+template <int D>
+__device__ __forceinline__ void merge_segment(const DecodeParams &p, int b, int h, int64_t k0,
+                                              int n, int nthreads) {
+    const int RG = p.R * p.G;
+    const auto ro = rows_rsrc(p.part_o + k0 * RG * D, (int64_t)n * RG * D);
+    const auto rl = rows_rsrc(p.part_lse + k0 * RG, (int64_t)n * RG);
+    for (int e = 4 * threadIdx.x; e < RG * D; e += 4 * nthreads) {
+        const int c = e / D, d = e % D;
+        float M = kNegInf, W = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < n; k += kMergeUnroll) {
+            float l[kMergeUnroll];
+            f32x4 o[kMergeUnroll];
+#pragma unroll
+            for (int u = 0; u < kMergeUnroll; ++u) {   // past n: no weight (o reads 0)
+                const int kk = k + u;
+                l[u] = kk < n ? fetch(rl, 4u * (uint32_t)(kk * RG + c)) : kNegInf;
+                o[u] = fetch4(ro, 4u * (uint32_t)((kk * RG + c) * D + d));
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeUnroll; ++u) {
+                if (l[u] == kNegInf) continue;
+                const float M2 = fmaxf(M, l[u]);
+                const float a = __expf(M - M2), w = __expf(l[u] - M2);   // M = -inf: a = 0
+                W = W * a + w;
+                acc = acc * a + w * o[u];
+                M = M2;
+            }
+        }
+        if (M != kNegInf) acc = acc * (1.0f / W);
+        const int64_t row = out_row(p, b, h, c);
+        store_bf16x4(p.out, row * D + d, acc);
+        if (p.out_lse && d == 0) p.out_lse[row] = M == kNegInf ? kNegInf : M + __logf(W);
+    }
+}
+
+// After a workgroup wrote the partial of its descriptor in segment (b, h)
+// (all threads): take a ticket; the last one merges.  `last` is LDS.
+template <int D>
+__device__ __forceinline__ void ticket_and_merge(const DecodeParams &p, int b, int h,
+                                                 int64_t k0, int n, int &last, int nthreads) {
+    const int s = b * p.Hkv + h;
+    // Every wave's partial stores (agent-scope atomics) have completed
+    // (s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)) before the ticket is taken.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(p.tickets + s, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+    __syncthreads();
+    if (last) {
+        merge_segment<D>(p, b, h, k0, n, nthreads);
+        if (threadIdx.x == 0) p.tickets[s] = 0;
+    }
+}
+
+// Segments with no chunk (an empty request) get out = 0, lse = -inf from
+// workgroup s mod P, before its bin (all threads).
+template <int D>
+__device__ __forceinline__ void clear_empty_segments(const DecodeParams &p, int nthreads) {
+    const MapLayout lay(p.B, p.Hkv, p.P);
+    const int S = p.B * p.Hkv, RG = p.R * p.G;
+    for (int s = blockIdx.x; s < S; s += p.P) {
+        if (sload(p.map + lay.seg_off, s + 1) != sload(p.map + lay.seg_off, s)) continue;
+        const int b = s / p.Hkv, h = s % p.Hkv;
+        for (int e = 4 * threadIdx.x; e < RG * D; e += 4 * nthreads) {
+            const int c = e / D, d = e % D;
+            const int64_t row = out_row(p, b, h, c);
+            store_bf16x4(p.out, row * D + d, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (p.out_lse && d == 0) p.out_lse[row] = kNegInf;
+        }
+    }
+}
+
+// The chunk count of segment (b, h) and its first partial slot, when the
+// combine is fused (n = 0 otherwise).
+template <bool FU>
+__device__ __forceinline__ int seg_chunks(const DecodeParams &p, int b, int h, int64_t &k0) {
+    k0 = 0;
+    if constexpr (!FU) return 0;
+    const MapLayout lay(p.B, p.Hkv, p.P);
+    const int s = b * p.Hkv + h;
+    k0 = sload(p.map + lay.seg_off, s);
+    return sload(p.map + lay.seg_off, s + 1) - (int)k0;
+}
+
 // Merge the waves' states and write partial slot `slot` (R G rows).  All
 // threads.
-template <int D, int GR, int NCB, bool MR, class Between>
+template <int D, int GR, int NCB, bool MR, bool FU, class Between>
 __device__ __forceinline__ void merge_write(const DecodeParams &p, State<D, NCB> &st,
-                                            MergeLds<D, GR, NCB> &sm, int64_t slot,
+                                            MergeLds<D, GR, NCB> &sm, int64_t slot, int b, int h,
                                             const Lane &ln, Between between) {
     const int RG = rows_per_req<MR>(p) * p.G;
+    int64_t k0;
+    const int nch = seg_chunks<FU>(p, b, h, k0);   // fused combine: where the rows go
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int c0 = 16 * cb;
@@ -493,9 +651,10 @@ __device__ __forceinline__ void merge_write(const DecodeParams &p, State<D, NCB>
             for (int i = 0; i < 4; ++i) {
                 float *dst = &sm.o[ln.w][ln.r][(4 * ln.grp + i) * (D / 16)];
 #pragma unroll
-                for (int b = 0; b < D / 16; b += 4)
-                    *reinterpret_cast<f32x4 *>(dst + b) = f32x4{
-                        st.o[cb][b][i], st.o[cb][b + 1][i], st.o[cb][b + 2][i], st.o[cb][b + 3][i]};
+                for (int blk = 0; blk < D / 16; blk += 4)
+                    *reinterpret_cast<f32x4 *>(dst + blk) =
+                        f32x4{st.o[cb][blk][i], st.o[cb][blk + 1][i], st.o[cb][blk + 2][i],
+                              st.o[cb][blk + 3][i]};
             }
         }
         __syncthreads();
@@ -516,15 +675,30 @@ __device__ __forceinline__ void merge_write(const DecodeParams &p, State<D, NCB>
                 }
                 acc = acc * (1.0f / wsum);
             }
+            const float lse = M == kNegInf ? kNegInf : (M + log2f(wsum)) * kLn2;
+            if (nch == 1) {   // the segment's only chunk: its partial is the output
+                const int64_t row = out_row(p, b, h, c0 + g);
+                store_bf16x4(p.out, row * D + d, acc);
+                if (p.out_lse && d == 0) p.out_lse[row] = lse;
+                continue;
+            }
             // the slot's rows start at a uniform address, plus a 32-bit offset
             char *obase = reinterpret_cast<char *>(p.part_o + slot * RG * D);
-            *reinterpret_cast<f32x4 *>(obase + 4u * (uint32_t)((c0 + g) * D + d)) = acc;
-            if (d == 0)
-                p.part_lse[slot * RG + c0 + g] =
-                    M == kNegInf ? kNegInf : (M + log2f(wsum)) * kLn2;
+            float *dst = reinterpret_cast<float *>(obase + 4u * (uint32_t)((c0 + g) * D + d));
+            if constexpr (FU) {   // merged by another workgroup
+                publish4(rows_rsrc(p.part_o + slot * RG * D, (int64_t)RG * D),
+                         4u * (uint32_t)((c0 + g) * D + d), acc);
+                if (d == 0)
+                    publish(rows_rsrc(p.part_lse + slot * RG, RG), 4u * (uint32_t)(c0 + g), lse);
+            } else {
+                *reinterpret_cast<f32x4 *>(dst) = acc;
+                if (d == 0) p.part_lse[slot * RG + c0 + g] = lse;
+            }
         }
         if (cb + 1 < NCB) __syncthreads();   // the next block reuses sm.o
     }
+    if constexpr (FU)
+        if (nch > 1) ticket_and_merge<D>(p, b, h, k0, nch, sm.last, kDecodeThreads);
     between();   // e.g. stage the next descriptor's Q: no wave reads it now
     __syncthreads();
 }
@@ -538,16 +712,6 @@ struct Pos {
     int b, h, t, t1, L;
 };
 
-// Wave-uniform by construction (same address for every lane): keep it in a
-// scalar register so tile bases use the scalar-base load form.
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// A read-only int32 at a wave-uniform index, through the scalar memory path
-// (constant address space): its wait counts scalar loads only, so it never
-// waits for the KV tiles in flight on the vector memory path.
-__device__ __forceinline__ int sload(const int32_t *base, int64_t i) {
-    return ((const __attribute__((address_space(4))) int32_t *)base)[i];
-}
 
 // Field-wise select (a whole-struct ?: would be lowered through memory).
 __device__ __forceinline__ Pos pick(bool c, const Pos &a, const Pos &b) {
@@ -630,7 +794,7 @@ __device__ __forceinline__ Cols<NCB> columns(const DecodeParams &p, const Lane &
 // i + 1 (across descriptor boundaries) is being loaded into the other
 // register buffer.  The run starts at `first` and ends with descriptor
 // d_end - 1; partials go to slot d (by_desc) or to slot_base.
-template <class KV, int D, int GR, int NCB, bool MR>
+template <class KV, int D, int GR, int NCB, bool MR, bool FU>
 __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB> &sm,
                                       const MapSource &src, const Pos &first, int d_end,
                                       int64_t slot_base, bool by_desc) {
@@ -668,7 +832,8 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
         attend_tile<KV, D, NCB, MR>(p, sm.q, qs, now, nv_cur, cols, st, ln);
 
         if (!more || n.d != cur.d) {
-            merge_write<D, GR, NCB, MR>(p, st, sm, by_desc ? (int64_t)cur.d : slot_base, ln,
+            merge_write<D, GR, NCB, MR, FU>(p, st, sm, by_desc ? (int64_t)cur.d : slot_base, cur.b,
+                                        cur.h, ln,
                                         [&] {
                                             if (more) stage_q<KV, D, GR, NCB, MR>(p, sm, n.b, n.h);
                                         });
@@ -887,9 +1052,10 @@ __device__ __forceinline__ void write_columns(const DecodeParams &p, const State
     for (int i = 0; i < 4; ++i) {
         const uint32_t off = (uint32_t)(col * D + (4 * ln.grp + i) * (D / 16)) * 4u;
 #pragma unroll
-        for (int b = 0; b < D / 16; b += 4)
-            *reinterpret_cast<f32x4 *>(obase + off + 4 * b) =
-                f32x4{st.o[0][b][i], st.o[0][b + 1][i], st.o[0][b + 2][i], st.o[0][b + 3][i]} *
+        for (int blk = 0; blk < D / 16; blk += 4)
+            *reinterpret_cast<f32x4 *>(obase + off + 4 * blk) =
+                f32x4{st.o[0][blk][i], st.o[0][blk + 1][i], st.o[0][blk + 2][i],
+                      st.o[0][blk + 3][i]} *
                 inv;
     }
     if (ln.grp == 0)
@@ -984,17 +1150,18 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
 template <int NCB>
 constexpr int kDecodeWavesPerEu = NCB == 1 ? 3 : 2;
 
-template <class KV, int D, int GR, int NCB, bool MR>
+template <class KV, int D, int GR, int NCB, bool MR, bool FU>
 __global__ void __launch_bounds__(kDecodeThreads)
 __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<NCB>)))
 decode_kernel(DecodeParams p) {
     __shared__ MergeLds<D, GR, NCB> sm;
+    if constexpr (FU) clear_empty_segments<D>(p, kDecodeThreads);
     const MapLayout lay(p.B, p.Hkv, p.P);
     const int32_t *bin_off = p.map + lay.bin_off;
     const int d0 = uniform(bin_off[blockIdx.x]), d1 = uniform(bin_off[blockIdx.x + 1]);
     if (d0 >= d1) return;
     const MapSource src{p.map + lay.desc, p.map + lay.lens};
-    drain<KV, D, GR, NCB, MR>(p, sm, src, src.read(d0), d1, 0, true);
+    drain<KV, D, GR, NCB, MR, FU>(p, sm, src, src.read(d0), d1, 0, true);
 }
 
 template <class KV, int D, int GR, int NCB, bool MR>
@@ -1023,7 +1190,7 @@ static_decode_kernel(DecodeParams p) {
     }
     // The same drain as the dynamic kernel, over one range and no map: with
     // d_end = 1 and the range numbered 0 it never reads a descriptor.
-    drain<KV, D, GR, NCB, MR>(p, sm, MapSource{nullptr, nullptr},
+    drain<KV, D, GR, NCB, MR, false>(p, sm, MapSource{nullptr, nullptr},
                               Pos{0, b, h, (int)t0, (int)t1, L}, 1, slot, false);
 }
 
@@ -1082,7 +1249,7 @@ constexpr int shared_waves(int ncb) {
 
 template <class KV, int D, int NCB>
 hipError_t launch_shared(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
-    if (dynamic)
+    if (dynamic)   // (the fused combine is not offered for these workgroups)
         hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB), 0,
                            stream, p);
     else
@@ -1093,9 +1260,12 @@ hipError_t launch_shared(const DecodeParams &p, hipStream_t stream, bool dynamic
 
 template <class KV, int D, int GR, int NCB, bool MR>
 hipError_t launch_one(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
-    if (dynamic)
-        hipLaunchKernelGGL((decode_kernel<KV, D, GR, NCB, MR>), dim3(grid), dim3(kDecodeThreads),
-                           0, stream, p);
+    if (dynamic && p.out)
+        hipLaunchKernelGGL((decode_kernel<KV, D, GR, NCB, MR, true>), dim3(grid),
+                           dim3(kDecodeThreads), 0, stream, p);
+    else if (dynamic)
+        hipLaunchKernelGGL((decode_kernel<KV, D, GR, NCB, MR, false>), dim3(grid),
+                           dim3(kDecodeThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((static_decode_kernel<KV, D, GR, NCB, MR>), dim3(grid),
                            dim3(kDecodeThreads), 0, stream, p);
@@ -1139,8 +1309,8 @@ const void *decode_fn(int rows, int &threads) {
     threads = ncb == 1 ? kDecodeThreads : 64 * shared_waves<KV<D>, D>(ncb);
     switch (column_blocks(rows)) {
     case 1:
-        return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false>
-                         : (const void *)decode_kernel<KV<D>, D, 16, 1, false>;
+        return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false, false>
+                         : (const void *)decode_kernel<KV<D>, D, 16, 1, false, false>;
     case 2: return (const void *)decode_shared_kernel<KV<D>, D, 2>;
     case 3: return (const void *)decode_shared_kernel<KV<D>, D, shared_waves<KV<D>, D>(3)>;
     default: return (const void *)decode_shared_kernel<KV<D>, D, 4>;

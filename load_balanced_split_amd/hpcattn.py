@@ -86,6 +86,9 @@ _sig = {
     "hpcattn_decode": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims), _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, ctypes.POINTER(hpcattn_task_map), _vp, _vp,
                                       _i64, _vp]),
+    "hpcattn_decode_combine": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims), _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _vp, ctypes.POINTER(hpcattn_task_map),
+                                              _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
     "hpcattn_combine": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims),
                                        ctypes.POINTER(hpcattn_task_map), _vp, _vp, _vp, _vp,
                                        _vp]),
@@ -212,6 +215,21 @@ def hpcattn_decode(dims: hpcattn_dims, q, k_pages, v_pages, page_table, task_map
                                ctypes.byref(task_map.handle), _ptr(part_o), _ptr(part_lse),
                                rows, _stream(stream)),
            "hpcattn_decode")
+
+
+def hpcattn_decode_combine(dims: hpcattn_dims, q, k_pages, v_pages, page_table,
+                           task_map: TaskMap, part_o, part_lse, tickets, out, out_lse=None,
+                           q_scale=None, k_scale=None, v_scale=None, stream=None) -> None:
+    """Decode + combine in one launch; tickets: int32 [>= B * H_kv], zero."""
+    rows = part_o.shape[0] if hasattr(part_o, "shape") else 0
+    nt = tickets.numel() if hasattr(tickets, "numel") else 0
+    _check(_lib.hpcattn_decode_combine(ctypes.byref(dims), _ptr(q), _ptr(q_scale),
+                                       _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                       _ptr(v_scale), _ptr(page_table),
+                                       ctypes.byref(task_map.handle), _ptr(part_o),
+                                       _ptr(part_lse), rows, _ptr(tickets), nt, _ptr(out),
+                                       _ptr(out_lse), _stream(stream)),
+           "hpcattn_decode_combine")
 
 
 def hpcattn_combine(dims: hpcattn_dims, task_map: TaskMap, part_o, part_lse, out,

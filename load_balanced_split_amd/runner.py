@@ -46,6 +46,8 @@ class DecodeRunner:
         lead = w.q_shape(B)[:-1]
         self.out = torch.empty(lead + (self.D,), dtype=torch.bfloat16, device=device)
         self.out_lse = torch.empty(lead, dtype=torch.float32, device=device)
+        # tickets of the fused decode + combine: zero once, kept zero by it
+        self.tickets = torch.zeros(B * self.Hkv, dtype=torch.int32, device=device)
         self._static = {}
 
     def _kv(self, layer: int):
@@ -64,6 +66,15 @@ class DecodeRunner:
         H.hpcattn_decode(self.dims, self.prob.q, kv["k_pages"], kv["v_pages"], self.page_table,
                          self.task_map, self.part_o, self.part_lse, kv.get("q_scale"),
                          kv.get("k_scale"), kv.get("v_scale"), stream)
+
+    def decode_combine(self, layer: int = 0, stream=None):
+        """Decode + combine of one layer in one launch; returns (out, out_lse)."""
+        kv = self._kv(layer)
+        H.hpcattn_decode_combine(self.dims, self.prob.q, kv["k_pages"], kv["v_pages"],
+                                 self.page_table, self.task_map, self.part_o, self.part_lse,
+                                 self.tickets, self.out, self.out_lse, kv.get("q_scale"),
+                                 kv.get("k_scale"), kv.get("v_scale"), stream)
+        return self.out, self.out_lse
 
     def combine(self, stream=None):
         H.hpcattn_combine(self.dims, self.task_map, self.part_o, self.part_lse, self.out,

@@ -116,6 +116,24 @@ def test_decode_rejects_bad_arguments(H):
     assert _decode(H, _dims(H), small) == H.ERR_WORKSPACE
 
 
+def test_decode_combine_rejects_bad_arguments(H):
+    lib = H._lib
+    m = _map(H)   # B = 4, H_kv = 1, P = 8
+
+    def dc(dims, tickets=FAKE, nt=4, out=FAKE, rows=1 << 20, mp=m):
+        return lib.hpcattn_decode_combine(ctypes.byref(dims), FAKE, None, FAKE, FAKE, None, None,
+                                          FAKE, ctypes.byref(mp), FAKE, FAKE, rows, tickets, nt,
+                                          out, None, None)
+
+    assert dc(_dims(H), tickets=None) == H.ERR_NULL
+    assert dc(_dims(H), out=None) == H.ERR_NULL
+    assert dc(_dims(H), nt=3) == H.ERR_WORKSPACE          # fewer tickets than B * H_kv
+    assert dc(_dims(H), rows=4 + 8 - 2) == H.ERR_WORKSPACE
+    assert dc(_dims(H, batch=5)) == H.ERR_SHAPE
+    assert dc(_dims(H, q_rows=0)) == H.ERR_SHAPE
+    assert dc(_dims(H, kv_dtype=H.KV_FP8_E4M3)) == H.ERR_DTYPE
+
+
 def test_combine_and_static_reject_bad_arguments(H):
     lib = H._lib
     m = _map(H)
