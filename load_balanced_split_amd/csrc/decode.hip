@@ -743,6 +743,23 @@ __device__ __forceinline__ bool advance(const MapSource &src, int d_end, const P
     return same || next;
 }
 
+// The walk with the next descriptor read ahead: `pre` is the first tile of
+// descriptor x.d + 1, read when descriptor x.d was entered, so that crossing
+// a descriptor boundary waits for no descriptor read (only the page id).
+// Past the run's last descriptor it repeats that one (a valid read); runs
+// without a map (the static kernel) have a single range and read nothing.
+__device__ __forceinline__ Pos read_ahead(const MapSource &src, int d_end, const Pos &x) {
+    return src.desc ? src.read(min(x.d + 1, d_end - 1)) : x;
+}
+
+__device__ __forceinline__ bool advance_ahead(int d_end, const Pos &x, const Pos &pre, Pos &y) {
+    const bool same = x.t + 1 < x.t1;
+    Pos n = x;
+    n.t = x.t + 1;
+    y = pick(same, n, pre);
+    return same || x.d + 1 < d_end;
+}
+
 // Page id of the tile at x and the request's tokens from the tile's first
 // on (nv, not clamped to 64: a query row that sees lag fewer tokens than the
 // request holds needs nv - lag); a tile outside the page table or with a
@@ -812,6 +829,7 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
     float qs[NCB];
     q_scale_of<KV, NCB, MR>(p, cur, cols, qs);
     st.reset();
+    Pos pre = read_ahead(src, d_end, cur);
     Tile ta, tb;
     const int pg = locate(p, cur, nv_cur);
     KV::load_tile(p, pg, cur.h, ln, ta);
@@ -823,7 +841,7 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
     // LDS inside the merge's barriers.
     auto step = [&](Tile &now, Tile &nxt) __attribute__((always_inline)) -> bool {
         Pos n;
-        const bool more = advance(src, d_end, cur, n);
+        const bool more = advance_ahead(d_end, cur, pre, n);
         const Pos far = pick(more, n, cur);
         int nv_n;
         const int pg_n = locate(p, far, nv_n);
@@ -838,6 +856,7 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
                                             if (more) stage_q<KV, D, GR, NCB, MR>(p, sm, n.b, n.h);
                                         });
             if (!more) return false;
+            pre = read_ahead(src, d_end, n);
             q_scale_of<KV, NCB, MR>(p, n, cols, qs);
             st.reset();
         }
@@ -1112,6 +1131,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
     typename KV::Q q;
     Pos cur = first;
     int nv_cur;
+    Pos pre = read_ahead(src, d_end, cur);
     Staged<KV, D, NCB> stg;
     stage_load<KV, D, NCB>(p, locate(p, cur, nv_cur), cur.h, stg);
     load_q_direct<KV>(p, cur, col, ln, q);
@@ -1122,7 +1142,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
 
     while (true) {
         Pos n;
-        const bool more = advance(src, d_end, cur, n);
+        const bool more = advance_ahead(d_end, cur, pre, n);
         const Pos far = pick(more, n, cur);
         int nv_n;
         stage_load<KV, D, NCB>(p, locate(p, far, nv_n), far.h, stg);
@@ -1133,6 +1153,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         if (!more || n.d != cur.d) {
             write_columns<D>(p, st, 16 * ln.w, by_desc ? (int64_t)cur.d : slot_base, ln);
             if (!more) return;
+            pre = read_ahead(src, d_end, n);
             load_q_direct<KV>(p, n, col, ln, q);
             qs = q_scale_at(n);
             st.reset();
