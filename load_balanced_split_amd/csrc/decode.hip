@@ -9,23 +9,27 @@
 // the static scheme (fixed grid over KV heads x requests x chunks) that the
 // static kernel here reproduces.
 //
-// Work split on gfx950 (wave64, MFMA):
+// Two device paths.  The per-wave path (up to 16 query rows per KV head:
+// plain decode, G <= 16) is described here; the shared-tile path for more
+// rows (multi-row draft verification) is described at its own section.
+//
+// Work split on gfx950 (wave64, MFMA), per-wave path:
 //   * a workgroup is 4 waves; wave w owns tokens [16 w, 16 w + 16) of every
 //     tile, so all 4 waves stay busy even on one-tile descriptors and no
 //     barrier is needed inside a descriptor;
 //   * one K/V tile (64 tokens of one KV head) serves every query row of its
-//     group: the G query heads times the R rows of a multi-row (draft
-//     verify) step, R G <= 64, as NCB = ceil(R G / 16) blocks of 16 columns:
-//     S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,fp8} (16 tokens x 16
-//     columns per block), O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, the K
-//     and V operands shared by all blocks;
+//     group (G heads, times R rows of a multi-row step, R G <= 16) as 16 MFMA
+//     columns: S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,fp8} (16 tokens x 16
+//     columns), O^T += V^T P^T on v_mfma_f32_16x16x16_bf16;
 //   * K and V go straight from HBM to registers with 16-byte loads: lane
 //     (r = lane % 16, grp = lane / 16) reads token 16 w + r of K at a d-range
 //     that only has to match Q's, and tokens 16 w + 4 grp + j of V at
 //     d = r * D/16 .. + D/16, repacked to the MFMA operand with v_perm;
 //     these are nontemporal loads, since every KV byte is read once;
 //   * the next tile (across descriptor boundaries) is always in flight while
-//     the current one is computed;
+//     the current one is computed; page ids and descriptors are read through
+//     the scalar memory path (their waits do not count the KV loads), the
+//     next descriptor as soon as the current one is entered;
 //   * each wave keeps its own running max / sum / O; the 4 waves are merged
 //     in LDS at the end of a descriptor.
 // Scores are kept in log2 units (scaled by sm_scale * log2 e) and exp2 is
@@ -729,19 +733,6 @@ struct MapSource {
         return Pos{d, b, sload(desc, o + 1), sload(desc, o + 2), sload(desc, o + 3), sload(lens, b)};
     }
 };
-
-// y = the tile after x in drain order; false at the end of the run
-// (descriptors x.d + 1 .. d_end - 1 come from src).  y is written once, from
-// SSA values, so that the position stays in registers.
-__device__ __forceinline__ bool advance(const MapSource &src, int d_end, const Pos &x, Pos &y) {
-    const bool same = x.t + 1 < x.t1;
-    const bool next = !same && x.d + 1 < d_end;
-    Pos n = x;
-    n.t = x.t + 1;
-    if (next) n = src.read(x.d + 1);
-    y = n;
-    return same || next;
-}
 
 // The walk with the next descriptor read ahead: `pre` is the first tile of
 // descriptor x.d + 1, read when descriptor x.d was entered, so that crossing
