@@ -398,52 +398,53 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
-    # The timed region: K steps, replayed from a HIP graph (default) or
-    # launched eagerly.  A graph holds `per_graph` consecutive steps so that
-    # the one-layer workloads still rotate over their pools.
+    # The timed region: exactly K steps, enqueued back to back with no host
+    # synchronisation between them (as a serving loop enqueues its steps),
+    # bracketed by a synchronize on each side.  Graph mode replays a graph of
+    # `per_graph` consecutive steps, so that the one-layer workloads still
+    # rotate over their pools, and a one-step graph for any remainder.
+    # Events between replays give the spread of the per-step time.
     per_graph = 1 if layers >= pools else pools // layers
-    step_ms = []
-    wall0 = time.perf_counter()
-    if args.eager:
-        for k in range(args.steps):
-            a, b = events()
-            a.record(stream)
-            step(args.warmup + k)
-            b.record(stream)
-            b.synchronize()
-            step_ms.append(a.elapsed_time(b))
-    else:
-        g = capture(lambda: [step(k) for k in range(per_graph)])
-        g.replay()
+
+    def timed(one_step):
+        """(ms for all K steps, per-step ms of each replay, host seconds)."""
+        if args.eager:
+            chunks = [(lambda k=k: one_step(args.warmup + k), 1) for k in range(args.steps)]
+        else:
+            full, rem = divmod(args.steps, per_graph)
+            chunks = []
+            if full:
+                g = capture(lambda: [one_step(k) for k in range(per_graph)])
+                g.replay()
+                chunks += [(g.replay, per_graph)] * full
+            if rem:
+                g1 = capture(lambda: one_step(0))
+                g1.replay()
+                chunks += [(g1.replay, 1)] * rem
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(chunks) + 1)]
         torch.cuda.synchronize()
-        for _ in range(max(1, args.steps // per_graph)):
-            a, b = events()
-            a.record(stream)
-            g.replay()
-            b.record(stream)
-            b.synchronize()
-            step_ms.append(a.elapsed_time(b) / per_graph)
-    wall = time.perf_counter() - wall0
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for i, (run_chunk, _) in enumerate(chunks):
+            run_chunk()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        host_s = time.perf_counter() - t0
+        per = [evs[i].elapsed_time(evs[i + 1]) / n for i, (_, n) in enumerate(chunks)]
+        return evs[0].elapsed_time(evs[-1]), per, host_s
+
+    total_ms, step_ms, wall = timed(step)
+    t_step = total_ms / args.steps
 
     # The same step with decode and combine fused into one launch per layer
-    # (hpcattn_decode_combine), replayed the same way.
+    # (hpcattn_decode_combine), timed the same way.
     def fused_step(k):
         run.plan()
         for layer in range(layers):
             run.decode_combine((k * layers + layer) % pools)
 
-    gf = capture(lambda: [fused_step(k) for k in range(per_graph)])
-    gf.replay()
-    torch.cuda.synchronize()
-    fused_ms = []
-    for _ in range(max(1, args.steps // per_graph)):
-        a, b = events()
-        a.record(stream)
-        gf.replay()
-        b.record(stream)
-        b.synchronize()
-        fused_ms.append(a.elapsed_time(b) / per_graph)
-    med_fused = statistics.median(fused_ms)
+    total_fused_ms, _, _ = timed(fused_step)
+    t_fused = total_fused_ms / args.steps
 
     # Per-kernel GPU time, each kernel back to back in its own graph.
     n_dec = max(layers, pools) if multi_layer else pools
@@ -453,8 +454,7 @@ def main():
     plan_ms = graph_avg_ms(lambda: [run.plan() for _ in range(16)], 16)
     torch.cuda.synchronize()
 
-    med_step = statistics.median(step_ms)
-    value = kv_bytes_layer * layers / (med_step * 1e-3) / 1e9
+    value = kv_bytes_layer * layers / (t_step * 1e-3) / 1e9
     achieved = kv_bytes_layer / (dec_avg * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -463,8 +463,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(med_step, 4),
-        "us_per_step": round(med_step * 1e3, 1),
+        "ms_per_step": round(t_step, 4),
+        "us_per_step": round(t_step * 1e3, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -486,7 +486,7 @@ def main():
         "breakdown_us": {"plan": round(plan_ms * 1e3, 2),
                          "decode_avg": round(dec_avg * 1e3, 2),
                          "combine": round(combine_ms * 1e3, 2),
-                         "launch_gaps": round((med_step - plan_ms - layers * (dec_avg + combine_ms))
+                         "launch_gaps": round((t_step - plan_ms - layers * (dec_avg + combine_ms))
                                               * 1e3, 1),
                          "step_min": round(min(step_ms) * 1e3, 1),
                          "step_p90": round(sorted(step_ms)[int(0.9 * (len(step_ms) - 1))] * 1e3, 1)},
@@ -495,10 +495,10 @@ def main():
                      "traffic": traffic_from_profile(name),
                      "kernel": "%s (one launch = one layer's live KV)" % (
                          "decode_shared_kernel" if w.q_rows * w.group > 16 else "decode_kernel")},
-        "fused": {"us_per_step": round(med_fused * 1e3, 1),
-                  "gbs": round(kv_bytes_layer * layers / (med_fused * 1e-3) / 1e9, 2),
+        "fused": {"us_per_step": round(t_fused * 1e3, 1),
+                  "gbs": round(kv_bytes_layer * layers / (t_fused * 1e-3) / 1e9, 2),
                   "decode_combine_avg_us": round(fused_avg * 1e3, 2),
-                  "speedup_vs_two_launches": round(med_step / med_fused, 4)},
+                  "speedup_vs_two_launches": round(t_step / t_fused, 4)},
         "wall_s_timed": round(wall, 3),
         "launch": "eager" if args.eager else "hip_graph (%d step(s) per replay)" % per_graph,
     }
@@ -506,7 +506,7 @@ def main():
     if args.ablation:
         out["ablation"] = static_sweep(run, prob, layers, pools, stream, dec_avg)
     if w.q_rows > 1:
-        out["multi_row"] = rows_as_requests(prob, layers, pools, med_step, dec_avg, capture,
+        out["multi_row"] = rows_as_requests(prob, layers, pools, t_step, dec_avg, capture,
                                             graph_avg_ms, args)
 
     if not args.no_cpu_baseline:

@@ -1104,6 +1104,31 @@ __device__ __forceinline__ void load_q_direct(const DecodeParams &p, const Pos &
 // The drain loop of the shared-tile path (same descriptor walk as drain):
 // tile t + 1 is issued into registers before tile t is computed from LDS
 // and stored to LDS after it.
+// Wave priority from a bin's progress.  The SIMDs issue the oldest wave
+// first, so among the equal bins of one CU the workgroup that arrived first
+// finishes first and the last one runs its tail alone; a compute-heavy
+// kernel then runs that tail on a fraction of the CU.  A wave starts at
+// priority 3 and steps down by one after each quarter of q tiles (the size
+// of every bin, within one tile), so the waves that are behind issue first
+// and the bins of a CU end together.  All counters are wave-uniform, and
+// s_setprio takes an immediate.
+struct Fairness {
+    int quarter, left, level;
+    __device__ explicit Fairness(int q_tiles)
+        : quarter(max(1, q_tiles >> 2)), left(max(1, q_tiles >> 2)), level(3) {}
+    __device__ void start() const { __builtin_amdgcn_s_setprio(3); }
+    __device__ void tile() {
+        if (--left > 0 || level == 0) return;
+        left = quarter;
+        if (--level == 2)
+            __builtin_amdgcn_s_setprio(2);
+        else if (level == 1)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
+    }
+};
+
 template <class KV, int D, int NCB>
 __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV, D> &sm,
                                              const MapSource &src, const Pos &first, int d_end,
@@ -1130,6 +1155,12 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
     st.reset();
     stage_store<KV, D, NCB>(sm, stg);
     __syncthreads();
+    // The dynamic kernel's bins hold q tiles each (header word 2 of the map).
+    // The bf16 D = 128 four-wave instance sits at its register ceiling, where
+    // the counters would spill; it gained 0.5% from them and goes without.
+    constexpr bool kFair = !(NCB == 4 && D == 128 && !KV::kScaled);
+    Fairness fair(kFair && by_desc ? sload(p.map, 2) : 1 << 30);
+    if (kFair && by_desc) fair.start();
 
     while (true) {
         Pos n;
@@ -1138,6 +1169,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         int nv_n;
         stage_load<KV, D, NCB>(p, locate(p, far, nv_n), far.h, stg);
 
+        if (kFair && by_desc) fair.tile();
         attend_shared<KV, D>(p, sm, q, qs, nv_cur, col.lag, st, ln);
         __syncthreads();   // every wave is done with the tile in LDS
 
@@ -1259,11 +1291,41 @@ constexpr int shared_waves(int ncb) {
     return (ncb == 3 && !KV::kScaled && D == 128) ? 4 : ncb;
 }
 
+// Workgroups of three waves are held below what their registers allow, by
+// padding their LDS.  At three waves per SIMD the registers admit four per
+// CU (12 waves), but the dispatcher does not always find SIMDs with room for
+// every wave of the fourth: in a launch sized for four per CU some
+// workgroups then start only when another ends, and the launch takes up to
+// 1.5 times as long.  k = (4 occ - 3) / 3 workgroups leave room for any
+// placement of one more workgroup's waves: three at three waves per SIMD,
+// four at four.  Computed once per instance from its register count.
+constexpr int kLdsPerCu = 160 * 1024;
+
+template <class KV, int D, int NCB>
+unsigned shared_lds_pad() {
+    if constexpr (NCB != 3) {
+        return 0u;
+    } else {
+        static const unsigned pad = [] {
+            hipFuncAttributes a{};
+            if (hipFuncGetAttributes(&a, (const void *)decode_shared_kernel<KV, D, 3>) !=
+                hipSuccess)
+                return 0u;
+            const int regs = (max(a.numRegs, 1) + 7) / 8 * 8;   // allocation granule
+            const int occ = min(8, 512 / regs);                  // waves per SIMD
+            const int k = max(1, (4 * occ - 3) / 3);
+            const int want = kLdsPerCu / k - (int)sizeof(SharedLds<KV, D>);
+            return want > 0 ? (unsigned)want & ~1023u : 0u;
+        }();
+        return pad;
+    }
+}
+
 template <class KV, int D, int NCB>
 hipError_t launch_shared(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
     if (dynamic)   // (the fused combine is not offered for these workgroups)
-        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB), 0,
-                           stream, p);
+        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB),
+                           (shared_lds_pad<KV, D, NCB>()), stream, p);
     else
         hipLaunchKernelGGL((static_decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB),
                            0, stream, p);
@@ -1316,9 +1378,10 @@ hipError_t dispatch(const DecodeParams &p, int head_dim, int kv_dtype, hipStream
 // The dynamic kernel launch_for picks for `rows` rows with R = 1 when
 // rows <= 16 (the resident count does not depend on R otherwise).
 template <template <int> class KV, int D>
-const void *decode_fn(int rows, int &threads) {
+const void *decode_fn(int rows, int &threads, unsigned &lds_pad) {
     const int ncb = column_blocks(rows);
     threads = ncb == 1 ? kDecodeThreads : 64 * shared_waves<KV<D>, D>(ncb);
+    lds_pad = threads == 3 * 64 ? shared_lds_pad<KV<D>, D, 3>() : 0u;
     switch (column_blocks(rows)) {
     case 1:
         return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false, false>
@@ -1334,12 +1397,13 @@ const void *decode_fn(int rows, int &threads) {
 int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t rows) {
     int n = 0;
     int threads = 0;
+    unsigned pad = 0;
     const void *fn = kv_dtype == HPCATTN_KV_BF16
-                         ? (head_dim == 128 ? decode_fn<Bf16, 128>(rows, threads)
-                                            : decode_fn<Bf16, 64>(rows, threads))
-                         : (head_dim == 128 ? decode_fn<Fp8, 128>(rows, threads)
-                                            : decode_fn<Fp8, 64>(rows, threads));
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess)
+                         ? (head_dim == 128 ? decode_fn<Bf16, 128>(rows, threads, pad)
+                                            : decode_fn<Bf16, 64>(rows, threads, pad))
+                         : (head_dim == 128 ? decode_fn<Fp8, 128>(rows, threads, pad)
+                                            : decode_fn<Fp8, 64>(rows, threads, pad));
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, pad) != hipSuccess)
         return 0;
     return n;
 }
