@@ -798,6 +798,33 @@ __device__ __forceinline__ Cols<NCB> columns(const DecodeParams &p, const Lane &
     return c;
 }
 
+// Wave priority from a bin's progress.  The SIMDs issue the oldest wave
+// first, so among the equal bins of one CU the workgroup that arrived first
+// finishes first and the last one runs its tail alone, on a fraction of the
+// CU's issue slots.  That tail costs the compute-heavy multi-row kernels a
+// few percent; the one-row kernel gains 1% on mixed lengths from evening it
+// out and loses 0.5% on a few long requests among many short.  A wave starts at
+// priority 3 and steps down by one after each quarter of q tiles (the size
+// of every bin, within one tile), so the waves that are behind issue first
+// and the bins of a CU end together.  All counters are wave-uniform, and
+// s_setprio takes an immediate.
+struct Fairness {
+    int quarter, left, level;
+    __device__ explicit Fairness(int q_tiles)
+        : quarter(max(1, q_tiles >> 2)), left(max(1, q_tiles >> 2)), level(3) {}
+    __device__ void start() const { __builtin_amdgcn_s_setprio(3); }
+    __device__ void tile() {
+        if (--left > 0 || level == 0) return;
+        left = quarter;
+        if (--level == 2)
+            __builtin_amdgcn_s_setprio(2);
+        else if (level == 1)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
+    }
+};
+
 // Drains a run of descriptors tile by tile: while tile i is computed, tile
 // i + 1 (across descriptor boundaries) is being loaded into the other
 // register buffer.  The run starts at `first` and ends with descriptor
@@ -825,6 +852,8 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
     const int pg = locate(p, cur, nv_cur);
     KV::load_tile(p, pg, cur.h, ln, ta);
     __syncthreads();
+    Fairness fair(by_desc ? sload(p.map, 2) : 1 << 30);   // bins of q tiles (map word 2)
+    if (by_desc) fair.start();
 
     // Issue tile i + 1 into `nxt` (after the last tile, a repeat of it that
     // keeps the steady-state path branch-free), compute tile i from `now`,
@@ -838,6 +867,7 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
         const int pg_n = locate(p, far, nv_n);
         KV::load_tile(p, pg_n, far.h, ln, nxt);
 
+        if (by_desc) fair.tile();
         attend_tile<KV, D, NCB, MR>(p, sm.q, qs, now, nv_cur, cols, st, ln);
 
         if (!more || n.d != cur.d) {
@@ -1104,31 +1134,6 @@ __device__ __forceinline__ void load_q_direct(const DecodeParams &p, const Pos &
 // The drain loop of the shared-tile path (same descriptor walk as drain):
 // tile t + 1 is issued into registers before tile t is computed from LDS
 // and stored to LDS after it.
-// Wave priority from a bin's progress.  The SIMDs issue the oldest wave
-// first, so among the equal bins of one CU the workgroup that arrived first
-// finishes first and the last one runs its tail alone; a compute-heavy
-// kernel then runs that tail on a fraction of the CU.  A wave starts at
-// priority 3 and steps down by one after each quarter of q tiles (the size
-// of every bin, within one tile), so the waves that are behind issue first
-// and the bins of a CU end together.  All counters are wave-uniform, and
-// s_setprio takes an immediate.
-struct Fairness {
-    int quarter, left, level;
-    __device__ explicit Fairness(int q_tiles)
-        : quarter(max(1, q_tiles >> 2)), left(max(1, q_tiles >> 2)), level(3) {}
-    __device__ void start() const { __builtin_amdgcn_s_setprio(3); }
-    __device__ void tile() {
-        if (--left > 0 || level == 0) return;
-        left = quarter;
-        if (--level == 2)
-            __builtin_amdgcn_s_setprio(2);
-        else if (level == 1)
-            __builtin_amdgcn_s_setprio(1);
-        else
-            __builtin_amdgcn_s_setprio(0);
-    }
-};
-
 template <class KV, int D, int NCB>
 __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV, D> &sm,
                                              const MapSource &src, const Pos &first, int d_end,
