@@ -24,6 +24,7 @@ namespace hpcattn {
 namespace {
 
 constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kWaveChunks = 32;   // segments with more descriptors are written by a wave
 
 struct Bins {
     int64_t T, P_eff, q, r;
@@ -31,12 +32,21 @@ struct Bins {
     __device__ int64_t start(int64_t i) const {
         return i <= P_eff ? i * q + (i < r ? i : r) : T;
     }
-    // Bin that owns global tile x, 0 <= x < T (then q >= 1).
+    // Bin that owns global tile x, 0 <= x < T (then q >= 1).  T fits in 31
+    // bits (a larger total is refused), so 32-bit division suffices.
     __device__ int64_t of(int64_t x) const {
         const int64_t big = r * (q + 1);
-        return x < big ? x / (q + 1) : r + (x - big) / q;
+        return x < big ? (uint32_t)x / (uint32_t)(q + 1)
+                       : r + (uint32_t)(x - big) / (uint32_t)q;
     }
 };
+
+// Lane l's value of v, l uniform across the wave (read into scalar registers).
+__device__ inline int64_t lane_value(int64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ int64_t wave_inclusive_scan(int64_t v) {
     const int lane = threadIdx.x & 63;
@@ -73,7 +83,7 @@ __device__ inline int64_t tiles_of(int32_t len) {
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_t P,
             int32_t m, int32_t *__restrict__ map) {
-    __shared__ int32_t s_cum[HPCATTN_MAX_BATCH];
+    __shared__ int32_t s_cum[HPCATTN_MAX_BATCH + 1];   // tiles before request b; [B] = all
     __shared__ int64_t s_wave[kPlanWaves];
     __shared__ int32_t s_err;
 
@@ -105,6 +115,7 @@ plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_
         s_cum[b] = (int32_t)run;
         run += tiles_of(seq_lens[b]);
     }
+    if (tid == 0) s_cum[B] = (int32_t)n_total;   // (meaningless on overflow, then unused)
     bool overflow = n_total * Hkv > (int64_t)INT32_MAX;
     if (overflow && tid == 0) s_err = HPCATTN_MAPERR_OVERFLOW;
     __syncthreads();
@@ -119,43 +130,73 @@ plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_
     bins.q = bins.T / bins.P_eff;
     bins.r = bins.T % bins.P_eff;
 
-    // Phase C: chunk count of every segment and their exclusive scan.
+    // Phase C: chunk count of every segment and their exclusive scan, over
+    // per_s consecutive segments per thread.
     const int64_t per_s = (S + kPlanThreads - 1) / kPlanThreads;
     const int64_t s0 = tid * per_s, s1 = min(S, s0 + per_s);
+    // Segment s: request b, head h, global tiles [st, en), first bin j0 and
+    // chunk count c.  s < 2^31 (larger sizes are refused).
+    struct Seg {
+        int b, h;
+        int64_t st, en, j0, c;
+    };
+    auto seg = [&](int64_t s) -> Seg {
+        Seg g;
+        g.b = (int)((uint32_t)s / (uint32_t)Hkv);
+        g.h = (int)((uint32_t)s - (uint32_t)g.b * (uint32_t)Hkv);
+        const int64_t n = s_cum[g.b + 1] - s_cum[g.b];
+        g.st = (int64_t)Hkv * s_cum[g.b] + g.h * n;
+        g.en = g.st + n;
+        g.j0 = n ? bins.of(g.st) : 0;
+        g.c = n ? bins.of(g.en - 1) - g.j0 + 1 : 0;
+        return g;
+    };
     local = 0;
-    if (!overflow) {
-        for (int64_t s = s0; s < s1; ++s) {
-            const int b = (int)(s / Hkv), h = (int)(s % Hkv);
-            const int64_t n = tiles_of(seq_lens[b]);
-            const int64_t st = (int64_t)Hkv * s_cum[b] + h * n;
-            local += n ? bins.of(st + n - 1) - bins.of(st) + 1 : 0;
-        }
-    }
+    if (!overflow)
+        for (int64_t s = s0; s < s1; ++s) local += seg(s).c;
     int64_t num_desc;
     run = block_exclusive_scan(local, &num_desc, s_wave);
 
-    // Phase D: per-segment offsets, descriptors, and the offset of every bin
-    // whose first tile opens a descriptor of this segment.
-    for (int64_t s = s0; s < s1; ++s) {
-        seg_off[s] = (int32_t)run;
-        if (overflow) continue;
-        const int b = (int)(s / Hkv), h = (int)(s % Hkv);
-        const int64_t n = tiles_of(seq_lens[b]);
-        if (!n) continue;
-        const int64_t st = (int64_t)Hkv * s_cum[b] + h * n, en = st + n;
-        const int64_t j0 = bins.of(st), c = bins.of(en - 1) - j0 + 1;
-        for (int64_t k = 0; k < c; ++k) {
-            const int64_t j = j0 + k;
-            const int64_t bs = bins.start(j), be = bins.start(j + 1);
-            const int64_t lo = bs > st ? bs : st, hi = be < en ? be : en;
-            int32_t *d4 = desc + 4 * (run + k);
-            d4[0] = b;
-            d4[1] = h;
-            d4[2] = (int32_t)(lo - st);
-            d4[3] = (int32_t)(hi - st);
-            if (k > 0 || st == bs) bin_off[j] = (int32_t)(run + k);
+    // Phase D: per-segment offsets and descriptors.  Each descriptor is the
+    // intersection of segment s with one bin j; a bin's first descriptor also
+    // sets its bin offset.  A thread writes the descriptors of its segment of
+    // the round; a segment of more than kWaveChunks (a single long request
+    // spans hundreds of bins) is written by the whole wave instead, a lane
+    // per descriptor, one such segment at a time.
+    auto put = [&](const Seg &g, int64_t i, int64_t d) {   // chunk i of g is descriptor d
+        const int64_t j = g.j0 + i, bs = bins.start(j), be = bins.start(j + 1);
+        const int64_t lo = bs > g.st ? bs : g.st, hi = be < g.en ? be : g.en;
+        int32_t *d4 = desc + 4 * d;
+        d4[0] = g.b;
+        d4[1] = g.h;
+        d4[2] = (int32_t)(lo - g.st);
+        d4[3] = (int32_t)(hi - g.st);
+        if (i > 0 || g.st == bs) bin_off[j] = (int32_t)d;
+    };
+    const int lane = tid & 63;
+    for (int64_t round = 0; round < per_s; ++round) {   // the same count in every wave
+        const int64_t s = s0 + round;
+        Seg g{0, 0, 0, 0, 0, 0};
+        if (s < s1) {
+            seg_off[s] = (int32_t)run;
+            if (!overflow) g = seg(s);
         }
-        run += c;
+        const bool wide = g.c > kWaveChunks;
+        if (!wide)
+            for (int64_t i = 0; i < g.c; ++i) put(g, i, run + i);
+        for (uint64_t longs = __ballot(wide); longs; longs &= longs - 1) {
+            const int l = __ffsll((unsigned long long)longs) - 1;   // wave-uniform
+            Seg w;
+            w.b = (int)lane_value(g.b, l);
+            w.h = (int)lane_value(g.h, l);
+            w.st = lane_value(g.st, l);
+            w.en = lane_value(g.en, l);
+            w.j0 = lane_value(g.j0, l);
+            w.c = lane_value(g.c, l);
+            const int64_t first = lane_value(run, l);
+            for (int64_t k = lane; k < w.c; k += 64) put(w, k, first + k);
+        }
+        run += g.c;
     }
     if (tid == 0) seg_off[S] = (int32_t)num_desc;
 
