@@ -960,22 +960,37 @@ __device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int 
 // K and V chunks go to row j / CPR, column j % CPR of the K-then-V rows
 // (CPR chunks per row); a round of T threads covers T / CPR whole rows, so
 // the address of round i is the thread's first address plus a constant.
+// fp8: in a tile with nv < 64 live tokens the V rows and v scales of the
+// dead slots (which may hold anything, NaN included) are stored as zeros, so
+// the P V product needs no masking (dead K rows are masked in the scores).
+// bf16 zeroes dead V in registers instead: the bf16 D = 128 kernel has no
+// register to spare for the staging-side form.
 template <class KV, int D, int NCB>
-__device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, NCB> &st) {
+__device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, NCB> &st,
+                                            int nv) {
     using S = Staged<KV, D, NCB>;
     constexpr int kRow = SharedLds<KV, D>::kRow, CPR = KV::kRowBytes / 16;
     static_assert(S::T % CPR == 0, "a round of chunks covers whole rows");
     uint8_t *base = sm.kv + (threadIdx.x / CPR) * kRow + 16 * (threadIdx.x % CPR);
+    const bool partial = KV::kScaled && nv < kTile;   // uniform
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
         const int j = threadIdx.x + S::T * i;
+        u32x4 c = st.c[i];
+        if (partial && j >= S::NK && j < 2 * S::NK && (j - S::NK) / CPR >= nv)
+            c = u32x4{0u, 0u, 0u, 0u};   // a dead V row
         if (S::T * (i + 1) <= 2 * S::NK) {   // a whole round of K / V chunks
-            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
+            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = c;
         } else if (j < 2 * S::NK) {
-            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
+            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = c;
         } else if (j < S::NT) {
-            const int q = j - 2 * S::NK;
-            *reinterpret_cast<u32x4 *>((q < 16 ? sm.ks : sm.vs) + 4 * (q & 15)) = st.c[i];
+            const int q = j - 2 * S::NK;   // 4 scales of tokens 4 (q & 15) ..
+            if (partial && q >= 16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * (q & 15) + e >= nv) c[e] = 0u;
+            }
+            *reinterpret_cast<u32x4 *>((q < 16 ? sm.ks : sm.vs) + 4 * (q & 15)) = c;
         }
     }
 }
@@ -1056,7 +1071,7 @@ __device__ __forceinline__ void attend_shared(const DecodeParams &p, const Share
             for (int j = 0; j < 8; ++j) {
                 const int tok = 32 * th + 16 * (j >> 2) + 4 * ln.grp + (j & 3);
                 KV::template v_part<VH>(sm.v() + tok * kRow, ln, c0, vv[j]);
-                if (nv < kTile && tok >= nv) {   // dead slots may hold NaN; P is 0 there
+                if (!KV::kScaled && nv < kTile && tok >= nv) {   // dead slots may hold NaN
 #pragma unroll
                     for (int c = 0; c < VH; ++c) vv[j][c] = 0u;
                 }
@@ -1158,7 +1173,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
     load_q_direct<KV>(p, cur, col, ln, q);
     float qs = q_scale_at(cur);
     st.reset();
-    stage_store<KV, D, NCB>(sm, stg);
+    stage_store<KV, D, NCB>(sm, stg, nv_cur);
     __syncthreads();
     // The dynamic kernel's bins hold q tiles each (header word 2 of the map).
     // The bf16 D = 128 four-wave instance sits at its register ceiling, where
@@ -1186,7 +1201,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
             qs = q_scale_at(n);
             st.reset();
         }
-        stage_store<KV, D, NCB>(sm, stg);
+        stage_store<KV, D, NCB>(sm, stg, nv_n);
         __syncthreads();   // tile t + 1 is in LDS
         cur = n;
         nv_cur = nv_n;
@@ -1386,7 +1401,7 @@ template <template <int> class KV, int D>
 const void *decode_fn(int rows, int &threads, unsigned &lds_pad) {
     const int ncb = column_blocks(rows);
     threads = ncb == 1 ? kDecodeThreads : 64 * shared_waves<KV<D>, D>(ncb);
-    lds_pad = threads == 3 * 64 ? shared_lds_pad<KV<D>, D, 3>() : 0u;
+    lds_pad = ncb == 3 ? shared_lds_pad<KV<D>, D, shared_waves<KV<D>, D>(3)>() : 0u;
     switch (column_blocks(rows)) {
     case 1:
         return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false, false>
