@@ -43,6 +43,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -202,16 +204,25 @@ struct Bf16 {
         }
     }
 
-    // Dwords c0 .. c0 + N - 1 of the lane's V run of one token.
-    template <int N>
-    __device__ static void v_part(const uint8_t *row, const Lane &ln, int c0, uint32_t (&w)[N]) {
-        const uint8_t *src = row + ln.r * (D / 16) * 2 + 4 * c0;
-        if constexpr (N == 2) {
-            const u32x2 x = *reinterpret_cast<const u32x2 *>(src);
-            w[0] = x[0]; w[1] = x[1];
-        } else {
-            w[0] = *reinterpret_cast<const uint32_t *>(src);
+    // The V^T operand of d-block blk for the shared-tile path, by two LDS
+    // transpose reads of 4 x bf16 each (ds_read_b64_tr_b16): within a group
+    // of 16 lanes, lane j receives element j % 4 of the rows that lanes
+    // 4 k + j / 4 point at, k = 0 .. 3.  Lane i of k-group g points at token
+    // tok(8 g + e), e = 4 h + i / 4 (read h), columns 16 blk + 4 (i % 4) ..,
+    // so lane j gets k-slots 8 g .. 8 g + 7 of d = 16 blk + j in k order.
+    template <class Tok>
+    __device__ static bf16x8 v_tr(const uint8_t *v, int row_bytes, int blk, const Lane &ln,
+                                  Tok tok) {
+        u32x2 h[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint8_t *a = v + tok(4 * half + (ln.r >> 2)) * row_bytes +
+                               2 * (16 * blk + 4 * (ln.r & 3));
+            h[half] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) v4i16 *)(a)));
         }
+        return __builtin_bit_cast(bf16x8, u32x4{h[0][0], h[0][1], h[1][0], h[1][1]});
     }
 
     // V^T operand of d-block blk: {V[t_j][r * D/16 + blk], j < 4} as bf16.
@@ -323,19 +334,27 @@ struct Fp8 {
         }
     }
 
-    // Dwords c0 .. c0 + N - 1 of the lane's widened V run of one token
-    // (dword c holds fp8 bytes 2 c, 2 c + 1 of the run as bf16).
-    template <int N>
-    __device__ static void v_part(const uint8_t *row, const Lane &ln, int c0, uint32_t (&w)[N]) {
-        const uint8_t *src = row + ln.r * (D / 16) + 2 * c0;
-        if constexpr (N == 2) {
-            const uint32_t x = *reinterpret_cast<const uint32_t *>(src);
-            w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
-            w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
-        } else {
-            const uint32_t x = *reinterpret_cast<const uint16_t *>(src);
-            w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+    // The V^T operand of d-block blk for the shared-tile path, by one LDS
+    // transpose read of 8 bytes (ds_read_b64_tr_b8): within a group of 16
+    // lanes, lane j receives byte j % 8 of the rows that lanes 2 k + j / 8
+    // point at, k = 0 .. 7.  Lane i of k-group g points at token
+    // tok(8 g + i / 2), bytes 16 blk + 8 (i % 2) .., so lane j gets k-slots
+    // 8 g .. 8 g + 7 of d = 16 blk + j in k order, widened here to bf16.
+    template <class Tok>
+    __device__ static bf16x8 v_tr(const uint8_t *v, int row_bytes, int blk, const Lane &ln,
+                                  Tok tok) {
+        const uint8_t *a = v + tok(ln.r >> 1) * row_bytes + 16 * blk + 8 * (ln.r & 1);
+        const v2i32 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i32 *)(a));
+        u32x4 w;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            w[2 * c] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[c], 1.0f, false));
+            w[2 * c + 1] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[c], 1.0f, true));
         }
+        return __builtin_bit_cast(bf16x8, w);
     }
 
     // Widen each token's D/16 fp8 values to bf16 (exact: every e4m3 value is
@@ -960,39 +979,39 @@ __device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int 
 // K and V chunks go to row j / CPR, column j % CPR of the K-then-V rows
 // (CPR chunks per row); a round of T threads covers T / CPR whole rows, so
 // the address of round i is the thread's first address plus a constant.
-// fp8: in a tile with nv < 64 live tokens the V rows and v scales of the
-// dead slots (which may hold anything, NaN included) are stored as zeros, so
-// the P V product needs no masking (dead K rows are masked in the scores).
-// bf16 zeroes dead V in registers instead: the bf16 D = 128 kernel has no
-// register to spare for the staging-side form.
 template <class KV, int D, int NCB>
-__device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, NCB> &st,
-                                            int nv) {
+__device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, NCB> &st) {
     using S = Staged<KV, D, NCB>;
     constexpr int kRow = SharedLds<KV, D>::kRow, CPR = KV::kRowBytes / 16;
     static_assert(S::T % CPR == 0, "a round of chunks covers whole rows");
     uint8_t *base = sm.kv + (threadIdx.x / CPR) * kRow + 16 * (threadIdx.x % CPR);
-    const bool partial = KV::kScaled && nv < kTile;   // uniform
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
         const int j = threadIdx.x + S::T * i;
-        u32x4 c = st.c[i];
-        if (partial && j >= S::NK && j < 2 * S::NK && (j - S::NK) / CPR >= nv)
-            c = u32x4{0u, 0u, 0u, 0u};   // a dead V row
         if (S::T * (i + 1) <= 2 * S::NK) {   // a whole round of K / V chunks
-            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = c;
+            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
         } else if (j < 2 * S::NK) {
-            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = c;
+            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
         } else if (j < S::NT) {
-            const int q = j - 2 * S::NK;   // 4 scales of tokens 4 (q & 15) ..
-            if (partial && q >= 16) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * (q & 15) + e >= nv) c[e] = 0u;
-            }
-            *reinterpret_cast<u32x4 *>((q < 16 ? sm.ks : sm.vs) + 4 * (q & 15)) = c;
+            const int q = j - 2 * S::NK;
+            *reinterpret_cast<u32x4 *>((q < 16 ? sm.ks : sm.vs) + 4 * (q & 15)) = st.c[i];
         }
     }
+}
+
+// The dead slots of a staged tile with nv < 64 live tokens (which may hold
+// anything, NaN included) get zero V rows and, for fp8, zero v scales, so
+// that P V needs no masking; dead K rows are masked in the scores.  All
+// threads; the caller brackets it with barriers.
+template <class KV, int D, int T>
+__device__ __forceinline__ void clear_dead(SharedLds<KV, D> &sm, int nv) {
+    constexpr int kRow = SharedLds<KV, D>::kRow, W = KV::kRowBytes / 16;
+    const int n0 = max(nv, 0);
+    uint8_t *v = sm.kv + kTile * kRow;
+    for (int i = threadIdx.x; i < (kTile - n0) * W; i += T)
+        *reinterpret_cast<u32x4 *>(v + (n0 + i / W) * kRow + 16 * (i % W)) = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (KV::kScaled)
+        for (int t = n0 + (int)threadIdx.x; t < kTile; t += T) sm.vs[t] = 0.f;
 }
 
 // One tile from LDS for the 16 columns of this wave's block, in two halves
@@ -1004,7 +1023,6 @@ __device__ __forceinline__ void attend_shared(const DecodeParams &p, const Share
                                               const typename KV::Q &q, float qs, int nv, int lag,
                                               State<D, 1> &st, const Lane &ln) {
     constexpr int kRow = SharedLds<KV, D>::kRow;
-    constexpr int VW = D / 32, VH = VW > 1 ? VW / 2 : 1;
     const bool masked = nv - (p.R - 1) < 2 * 32;   // some row sees < 64 tokens
     const int lim = nv - lag;
 #pragma unroll
@@ -1060,35 +1078,16 @@ __device__ __forceinline__ void attend_shared(const DecodeParams &p, const Share
         ps += __shfl_xor(ps, 32, 64);
         st.l[0] += ps;
 
-        // O^T += V^T P^T over the half's 32 tokens: k-slot e < 4 is token
-        // 32 th + 4 grp + e, e >= 4 token 32 th + 16 + 4 grp + e - 4.  V is
-        // read in halves of the lane's d-range (VH dwords of each token).
+        // O^T += V^T P^T over the half's 32 tokens: k-slot e < 4 of k-group
+        // g is token 32 th + 4 g + e, e >= 4 token 32 th + 16 + 4 g + e - 4
+        // (where the lane's P values sit); d-block blk covers d = 16 blk ..
+        // 16 blk + 15 (O^T row m is d = 16 blk + m).  Dead V rows are zero.
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        const auto tok = [&](int e) { return 32 * th + 16 * (e >> 2) + 4 * ln.grp + (e & 3); };
 #pragma unroll
-        for (int c0 = 0; c0 < VW; c0 += VH) {
-            uint32_t vv[8][VH];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int tok = 32 * th + 16 * (j >> 2) + 4 * ln.grp + (j & 3);
-                KV::template v_part<VH>(sm.v() + tok * kRow, ln, c0, vv[j]);
-                if (!KV::kScaled && nv < kTile && tok >= nv) {   // dead slots may hold NaN
-#pragma unroll
-                    for (int c = 0; c < VH; ++c) vv[j][c] = 0u;
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < VH; ++c) {
-                const u32x4 lo = {halves<false>(vv[0][c], vv[1][c]), halves<false>(vv[2][c], vv[3][c]),
-                                  halves<false>(vv[4][c], vv[5][c]), halves<false>(vv[6][c], vv[7][c])};
-                const u32x4 hi = {halves<true>(vv[0][c], vv[1][c]), halves<true>(vv[2][c], vv[3][c]),
-                                  halves<true>(vv[4][c], vv[5][c]), halves<true>(vv[6][c], vv[7][c])};
-                const int blk = 2 * (c0 + c);
-                st.o[0][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, lo), pb, st.o[0][blk], 0, 0, 0);
-                st.o[0][blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, hi), pb, st.o[0][blk + 1], 0, 0, 0);
-            }
-        }
+        for (int blk = 0; blk < D / 16; ++blk)
+            st.o[0][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                KV::v_tr(sm.v(), kRow, blk, ln, tok), pb, st.o[0][blk], 0, 0, 0);
     }
 }
 
@@ -1103,16 +1102,11 @@ __device__ __forceinline__ void write_columns(const DecodeParams &p, const State
     const bool live = st.l[0] > 0.f;
     const float inv = live ? 1.0f / st.l[0] : 0.f;
     char *obase = reinterpret_cast<char *>(p.part_o + slot * RG * D);
+    // accumulator blk holds d = 16 blk + 4 grp .. 16 blk + 4 grp + 3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (uint32_t)(col * D + (4 * ln.grp + i) * (D / 16)) * 4u;
-#pragma unroll
-        for (int blk = 0; blk < D / 16; blk += 4)
-            *reinterpret_cast<f32x4 *>(obase + off + 4 * blk) =
-                f32x4{st.o[0][blk][i], st.o[0][blk + 1][i], st.o[0][blk + 2][i],
-                      st.o[0][blk + 3][i]} *
-                inv;
-    }
+    for (int blk = 0; blk < D / 16; ++blk)
+        *reinterpret_cast<f32x4 *>(obase + (uint32_t)(col * D + 16 * blk + 4 * ln.grp) * 4u) =
+            st.o[0][blk] * inv;
     if (ln.grp == 0)
         p.part_lse[slot * RG + col] = live ? (st.m[0] + log2f(st.l[0])) * kLn2 : kNegInf;
 }
@@ -1173,8 +1167,12 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
     load_q_direct<KV>(p, cur, col, ln, q);
     float qs = q_scale_at(cur);
     st.reset();
-    stage_store<KV, D, NCB>(sm, stg, nv_cur);
+    stage_store<KV, D, NCB>(sm, stg);
     __syncthreads();
+    if (nv_cur < kTile) {
+        clear_dead<KV, D, 64 * NCB>(sm, nv_cur);
+        __syncthreads();
+    }
     // The dynamic kernel's bins hold q tiles each (header word 2 of the map).
     // The bf16 D = 128 four-wave instance sits at its register ceiling, where
     // the counters would spill; it gained 0.5% from them and goes without.
@@ -1201,8 +1199,12 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
             qs = q_scale_at(n);
             st.reset();
         }
-        stage_store<KV, D, NCB>(sm, stg, nv_n);
+        stage_store<KV, D, NCB>(sm, stg);
         __syncthreads();   // tile t + 1 is in LDS
+        if (nv_n < kTile) {
+            clear_dead<KV, D, 64 * NCB>(sm, nv_n);
+            __syncthreads();
+        }
         cur = n;
         nv_cur = nv_n;
     }
