@@ -1174,11 +1174,8 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         __syncthreads();
     }
     // The dynamic kernel's bins hold q tiles each (header word 2 of the map).
-    // The bf16 D = 128 four-wave instance sits at its register ceiling, where
-    // the counters would spill; it gained 0.5% from them and goes without.
-    constexpr bool kFair = !(NCB == 4 && D == 128 && !KV::kScaled);
-    Fairness fair(kFair && by_desc ? sload(p.map, 2) : 1 << 30);
-    if (kFair && by_desc) fair.start();
+    Fairness fair(by_desc ? sload(p.map, 2) : 1 << 30);
+    if (by_desc) fair.start();
 
     while (true) {
         Pos n;
@@ -1187,7 +1184,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         int nv_n;
         stage_load<KV, D, NCB>(p, locate(p, far, nv_n), far.h, stg);
 
-        if (kFair && by_desc) fair.tile();
+        if (by_desc) fair.tile();
         attend_shared<KV, D>(p, sm, q, qs, nv_cur, col.lag, st, ln);
         __syncthreads();   // every wave is done with the tile in LDS
 
