@@ -25,7 +25,9 @@
 //     (r = lane % 16, grp = lane / 16) reads token 16 w + r of K at a d-range
 //     that only has to match Q's, and tokens 16 w + 4 grp + j of V at
 //     d = r * D/16 .. + D/16, repacked to the MFMA operand with v_perm;
-//     these are nontemporal loads, since every KV byte is read once;
+//     these are nontemporal buffer loads (every KV byte is read once)
+//     bounded at the tile's live rows, so dead rows read as zero and cost
+//     no memory traffic;
 //   * the next tile (across descriptor boundaries) is always in flight while
 //     the current one is computed; page ids and descriptors are read through
 //     the scalar memory path (their waits do not count the KV loads), the
@@ -89,20 +91,60 @@ __device__ __forceinline__ T ldg(const void *base, uint32_t off) {
     return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
 }
 
-// KV is streamed once per layer: nontemporal loads keep it from displacing
-// reusable lines (Q, page ids, the task map) in the caches.
-template <class T>
-__device__ __forceinline__ T ldg_stream(const void *base, uint32_t off) {
-    return __builtin_nontemporal_load(
-        reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off));
-}
-
 // Start of the 64-token tile (page, h) of a [num_pages, H_kv, 64, D] pool
 // with `esize`-byte elements (uniform across the workgroup).
 __device__ __forceinline__ const char *tile_base(const void *pool, int page, int h, int Hkv,
                                                  int row_bytes) {
     return reinterpret_cast<const char *>(pool) +
            ((int64_t)page * Hkv + h) * (int64_t)kTile * row_bytes;
+}
+
+// Raw buffer resources (stride 0, word 3 of a plain untyped buffer).  A
+// dword of a buffer load at or past num_records bytes reads 0 without a
+// memory access, and a store there writes nothing.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kNontemporal = 2;   // cache policy nt: streamed once
+
+// `base` and `bytes` must be wave-uniform: they are read from the first
+// active lane, so that the resource lives in scalar registers (a resource
+// the compiler takes for divergent is used through a loop over its values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo),
+                                             (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                             kRawBufferWord3);
+}
+
+// The live rows of tile (page, h): tokens [0, live) of its 64, where `nv`
+// is the request's tokens from the tile's first on (clamped here).  Dead
+// rows read as zero and cost no HBM traffic; live = 0 reads nothing at all.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t live_rows(const void *pool, int page, int h,
+                                                             int Hkv, int row_bytes, int nv) {
+    const int live = min(max(nv, 0), kTile);
+    return span_rsrc(tile_base(pool, page, h, Hkv, row_bytes), live * row_bytes);
+}
+
+// A lane's byte offset, opaque to the optimiser at the point of use, so
+// that offset + constant folds into the load's immediate offset instead of
+// each sum being hoisted out of the loop into a register of its own.
+__device__ __forceinline__ uint32_t lane_off(uint32_t off) {
+    asm volatile("" : "+v"(off));
+    return off;
+}
+
+// Nontemporal buffer loads of 4, 2 or 1 dwords at a byte offset.  KV is
+// streamed once per layer: nontemporal loads keep it from displacing
+// reusable lines (Q, page ids, the task map) in the caches.
+__device__ __forceinline__ u32x4 ldb4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNontemporal);
+}
+__device__ __forceinline__ u32x2 ldb2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNontemporal);
+}
+__device__ __forceinline__ uint32_t ldb1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNontemporal);
 }
 
 // Wave-uniform by construction (same address for every lane): keep it in a
@@ -144,21 +186,24 @@ struct Bf16 {
             q.q[ks] = *reinterpret_cast<const u32x4 *>(sq + ln.r * stride + 16 * ks + 4 * ln.grp);
     }
 
-    __device__ static void load_tile(const DecodeParams &p, int page, int h, const Lane &ln,
-                                     Tile &t) {
-        const char *kb = tile_base(p.k, page, h, p.Hkv, D * 2);
-        const char *vb = tile_base(p.v, page, h, p.Hkv, D * 2);
-        const uint32_t koff = ((16 * ln.w + ln.r) * D + 8 * ln.grp) * 2;
+    // The wave's share of tile (page, h) with nv tokens from its first on:
+    // dead rows (token >= nv) read as zero.
+    __device__ static void load_tile(const DecodeParams &p, int page, int h, int nv,
+                                     const Lane &ln, Tile &t) {
+        const auto kr = live_rows(p.k, page, h, p.Hkv, D * 2, nv);
+        const auto vr = live_rows(p.v, page, h, p.Hkv, D * 2, nv);
+        const uint32_t koff = lane_off(((16 * ln.w + ln.r) * D + 8 * ln.grp) * 2);
+        const uint32_t voff = lane_off(((16 * ln.w + 4 * ln.grp) * D + ln.r * (D / 16)) * 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) t.k[ks] = ldg_stream<u32x4>(kb, koff + 64 * ks);
+        for (int ks = 0; ks < KS; ++ks) t.k[ks] = ldb4(kr, koff + 64 * ks);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t off = ((16 * ln.w + 4 * ln.grp + j) * D + ln.r * (D / 16)) * 2;
+            const uint32_t off = voff + j * D * 2;
             if constexpr (VW == 4) {
-                u32x4 x = ldg_stream<u32x4>(vb, off);
+                u32x4 x = ldb4(vr, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1]; t.v[j][2] = x[2]; t.v[j][3] = x[3];
             } else {
-                u32x2 x = ldg_stream<u32x2>(vb, off);
+                u32x2 x = ldb2(vr, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1];
             }
         }
@@ -261,27 +306,30 @@ struct Fp8 {
             q.q[c] = *reinterpret_cast<const u32x4 *>(sq + ln.r * stride + 16 * c + 4 * ln.grp);
     }
 
-    __device__ static void load_tile(const DecodeParams &p, int page, int h, const Lane &ln,
-                                     Tile &t) {
-        const char *kb = tile_base(p.k, page, h, p.Hkv, D);
-        const char *vb = tile_base(p.v, page, h, p.Hkv, D);
-        const uint32_t koff = (16 * ln.w + ln.r) * D + 16 * ln.grp;
+    // As for bf16; dead rows read as zero bytes and zero scales.
+    __device__ static void load_tile(const DecodeParams &p, int page, int h, int nv,
+                                     const Lane &ln, Tile &t) {
+        const auto kr = live_rows(p.k, page, h, p.Hkv, D, nv);
+        const auto vr = live_rows(p.v, page, h, p.Hkv, D, nv);
+        const uint32_t koff = lane_off((16 * ln.w + ln.r) * D + 16 * ln.grp);
+        const uint32_t voff = lane_off((16 * ln.w + 4 * ln.grp) * D + ln.r * (D / 16));
 #pragma unroll
-        for (int c = 0; c < NC; ++c) t.k[c] = ldg_stream<u32x4>(kb, koff + 64 * c);
+        for (int c = 0; c < NC; ++c) t.k[c] = ldb4(kr, koff + 64 * c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t off = (16 * ln.w + 4 * ln.grp + j) * D + ln.r * (D / 16);
+            const uint32_t off = voff + j * D;
             if constexpr (VB == 2) {
-                u32x2 x = ldg_stream<u32x2>(vb, off);
+                u32x2 x = ldb2(vr, off);
                 t.v[j][0] = x[0]; t.v[j][1] = x[1];
             } else {
-                t.v[j][0] = ldg_stream<uint32_t>(vb, off);
+                t.v[j][0] = ldb1(vr, off);
             }
         }
-        // Scales of tokens 16 w + 4 grp + i: one 16-byte run per lane group.
-        const uint32_t soff = (16 * ln.w + 4 * ln.grp) * 4;
-        t.ks = ldg_stream<f32x4>(tile_base(p.k_scale, page, h, p.Hkv, 4), soff);
-        t.vs = ldg_stream<f32x4>(tile_base(p.v_scale, page, h, p.Hkv, 4), soff);
+        // Scales of tokens 16 w + 4 grp + i: one 16-byte run per lane group
+        // (the bound is checked per dword).
+        const uint32_t soff = lane_off((16 * ln.w + 4 * ln.grp) * 4);
+        t.ks = __builtin_bit_cast(f32x4, ldb4(live_rows(p.k_scale, page, h, p.Hkv, 4, nv), soff));
+        t.vs = __builtin_bit_cast(f32x4, ldb4(live_rows(p.v_scale, page, h, p.Hkv, 4, nv), soff));
     }
 
     __device__ static f32x4 scores(const DecodeParams &p, const Q &q, const Tile &t,
@@ -454,15 +502,8 @@ __device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_
                                     u32x2{pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])});
     }
 
-    uint32_t vv[4][D / 32];
+    uint32_t vv[4][D / 32];   // dead rows were loaded as zero
     KV::v_dwords(t, vv);
-    if (nv < kTile) {   // dead slots may hold NaN: zero them, P is already 0
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (tok0 + j >= nv)
-#pragma unroll
-                for (int c = 0; c < D / 32; ++c) vv[j][c] = 0u;
-    }
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
         // d-blocks 2c and 2c + 1: low and high bf16 of dword c of each token.
@@ -537,11 +578,9 @@ __device__ __forceinline__ void store_bf16x4(void *out, int64_t elem, const f32x
 // L2 of an XCD) is needed around the ticket.  Out-of-range offsets read 0
 // and write nothing.
 constexpr int kCoherent = 16;          // cache policy: sc1
-constexpr int kRawBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const float *base, int64_t floats) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0,
-                                             (int)(floats * 4), kRawBufferWord3);
+    return span_rsrc(base, (int)(floats * 4));
 }
 
 __device__ __forceinline__ void publish4(__amdgpu_buffer_rsrc_t r, uint32_t byte, const f32x4 &v) {
@@ -869,22 +908,22 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
     Pos pre = read_ahead(src, d_end, cur);
     Tile ta, tb;
     const int pg = locate(p, cur, nv_cur);
-    KV::load_tile(p, pg, cur.h, ln, ta);
+    KV::load_tile(p, pg, cur.h, nv_cur, ln, ta);
     __syncthreads();
     Fairness fair(by_desc ? sload(p.map, 2) : 1 << 30);   // bins of q tiles (map word 2)
     if (by_desc) fair.start();
 
-    // Issue tile i + 1 into `nxt` (after the last tile, a repeat of it that
-    // keeps the steady-state path branch-free), compute tile i from `now`,
-    // close its descriptor if it ends, staging the next descriptor's Q in
-    // LDS inside the merge's barriers.
+    // Issue tile i + 1 into `nxt` (after the last tile, a load of no rows,
+    // which touches no memory and keeps the steady-state path branch-free),
+    // compute tile i from `now`, close its descriptor if it ends, staging
+    // the next descriptor's Q in LDS inside the merge's barriers.
     auto step = [&](Tile &now, Tile &nxt) __attribute__((always_inline)) -> bool {
         Pos n;
         const bool more = advance_ahead(d_end, cur, pre, n);
         const Pos far = pick(more, n, cur);
         int nv_n;
         const int pg_n = locate(p, far, nv_n);
-        KV::load_tile(p, pg_n, far.h, ln, nxt);
+        KV::load_tile(p, pg_n, far.h, more ? nv_n : 0, ln, nxt);
 
         if (by_desc) fair.tile();
         attend_tile<KV, D, NCB, MR>(p, sm.q, qs, now, nv_cur, cols, st, ln);
@@ -950,28 +989,38 @@ struct Staged {
 };
 
 template <class KV, int D, int NCB>
-__device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int h,
+__device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int h, int nv,
                                            Staged<KV, D, NCB> &st) {
     using S = Staged<KV, D, NCB>;
-    const char *kb = tile_base(p.k, page, h, p.Hkv, KV::kRowBytes);
-    const char *vb = tile_base(p.v, page, h, p.Hkv, KV::kRowBytes);
+    // Dead rows (token >= nv) and their scales read as zero.
+    const auto kr = live_rows(p.k, page, h, p.Hkv, KV::kRowBytes, nv);
+    const auto vr = live_rows(p.v, page, h, p.Hkv, KV::kRowBytes, nv);
+    __amdgpu_buffer_rsrc_t ksr = kr, vsr = vr;
+    if constexpr (KV::kScaled) {
+        ksr = live_rows(p.k_scale, page, h, p.Hkv, 4, nv);
+        vsr = live_rows(p.v_scale, page, h, p.Hkv, 4, nv);
+    }
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
         const int j = threadIdx.x + S::T * i;
         if (S::T * (i + 1) <= S::NK) {   // all K (a whole round of chunks)
-            st.c[i] = ldg_stream<u32x4>(kb, 16 * j);
+            st.c[i] = ldb4(kr, 16 * j);
         } else if (S::T * i >= S::NK && S::T * (i + 1) <= 2 * S::NK) {   // all V
-            st.c[i] = ldg_stream<u32x4>(vb, 16 * (j - S::NK));
+            st.c[i] = ldb4(vr, 16 * (j - S::NK));
         } else if (j < S::NT) {
-            const char *src;
-            if (j < S::NK)
-                src = kb + 16 * j;
-            else if (j < 2 * S::NK)
-                src = vb + 16 * (j - S::NK);
-            else
-                src = tile_base(j < 2 * S::NK + 16 ? p.k_scale : p.v_scale, page, h, p.Hkv, 4) +
-                      16 * ((j - 2 * S::NK) & 15);
-            st.c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+            // A round across K, V and the scales: a lane's chunk comes from
+            // one of them, and the loads from the others are given an offset
+            // past any tile (they read 0 and touch no memory), so that no
+            // resource depends on the lane.
+            constexpr uint32_t kOut = 1u << 20;
+            const auto pick = [&](bool mine, int chunk) { return mine ? 16u * chunk : kOut; };
+            u32x4 x = ldb4(kr, pick(j < S::NK, j)) |
+                      ldb4(vr, pick(j >= S::NK && j < 2 * S::NK, j - S::NK));
+            if constexpr (KV::kScaled) {
+                const int q = j - 2 * S::NK;
+                x |= ldb4(ksr, pick(q >= 0 && q < 16, q)) | ldb4(vsr, pick(q >= 16, q - 16));
+            }
+            st.c[i] = x;
         }
     }
 }
@@ -997,21 +1046,6 @@ __device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<K
             *reinterpret_cast<u32x4 *>((q < 16 ? sm.ks : sm.vs) + 4 * (q & 15)) = st.c[i];
         }
     }
-}
-
-// The dead slots of a staged tile with nv < 64 live tokens (which may hold
-// anything, NaN included) get zero V rows and, for fp8, zero v scales, so
-// that P V needs no masking; dead K rows are masked in the scores.  All
-// threads; the caller brackets it with barriers.
-template <class KV, int D, int T>
-__device__ __forceinline__ void clear_dead(SharedLds<KV, D> &sm, int nv) {
-    constexpr int kRow = SharedLds<KV, D>::kRow, W = KV::kRowBytes / 16;
-    const int n0 = max(nv, 0);
-    uint8_t *v = sm.kv + kTile * kRow;
-    for (int i = threadIdx.x; i < (kTile - n0) * W; i += T)
-        *reinterpret_cast<u32x4 *>(v + (n0 + i / W) * kRow + 16 * (i % W)) = u32x4{0u, 0u, 0u, 0u};
-    if constexpr (KV::kScaled)
-        for (int t = n0 + (int)threadIdx.x; t < kTile; t += T) sm.vs[t] = 0.f;
 }
 
 // One tile from LDS for the 16 columns of this wave's block, in two halves
@@ -1163,16 +1197,15 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
     int nv_cur;
     Pos pre = read_ahead(src, d_end, cur);
     Staged<KV, D, NCB> stg;
-    stage_load<KV, D, NCB>(p, locate(p, cur, nv_cur), cur.h, stg);
+    {
+        const int pg = locate(p, cur, nv_cur);
+        stage_load<KV, D, NCB>(p, pg, cur.h, nv_cur, stg);
+    }
     load_q_direct<KV>(p, cur, col, ln, q);
     float qs = q_scale_at(cur);
     st.reset();
     stage_store<KV, D, NCB>(sm, stg);
     __syncthreads();
-    if (nv_cur < kTile) {
-        clear_dead<KV, D, 64 * NCB>(sm, nv_cur);
-        __syncthreads();
-    }
     // The dynamic kernel's bins hold q tiles each (header word 2 of the map).
     Fairness fair(by_desc ? sload(p.map, 2) : 1 << 30);
     if (by_desc) fair.start();
@@ -1182,7 +1215,8 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         const bool more = advance_ahead(d_end, cur, pre, n);
         const Pos far = pick(more, n, cur);
         int nv_n;
-        stage_load<KV, D, NCB>(p, locate(p, far, nv_n), far.h, stg);
+        const int pg_n = locate(p, far, nv_n);
+        stage_load<KV, D, NCB>(p, pg_n, far.h, more ? nv_n : 0, stg);
 
         if (by_desc) fair.tile();
         attend_shared<KV, D>(p, sm, q, qs, nv_cur, col.lag, st, ln);
@@ -1198,10 +1232,6 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         }
         stage_store<KV, D, NCB>(sm, stg);
         __syncthreads();   // tile t + 1 is in LDS
-        if (nv_n < kTile) {
-            clear_dead<KV, D, 64 * NCB>(sm, nv_n);
-            __syncthreads();
-        }
         cur = n;
         nv_cur = nv_n;
     }
@@ -1227,6 +1257,9 @@ decode_kernel(DecodeParams p) {
     drain<KV, D, GR, NCB, MR, FU>(p, sm, src, src.read(d0), d1, 0, true);
 }
 
+// The static ablation keeps the compiler's register allocation (two
+// workgroups per CU at D = 128): its grid of many short workgroups ran
+// 1-2% faster that way than at the dynamic kernel's three per CU.
 template <class KV, int D, int GR, int NCB, bool MR>
 __global__ void __launch_bounds__(kDecodeThreads)
 static_decode_kernel(DecodeParams p) {

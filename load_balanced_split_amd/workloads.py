@@ -135,11 +135,12 @@ def quantize_e4m3(x: torch.Tensor):
 
 def poison_dead_slots(pool: torch.Tensor, lens: np.ndarray, pt: np.ndarray, value) -> None:
     """Fill the slots past each request's length in its last page with a NaN
-    pattern, so that any read of dead KV shows up in the output."""
+    pattern, so that any read of dead KV shows up in the output.  `pool` is a
+    KV pool [num_pages, Hkv, 64, D] or a scale pool [num_pages, Hkv, 64]."""
     for b, L in enumerate(np.asarray(lens)):
         L = int(L)
         if L % PAGE:
-            pool[int(pt[b, L // PAGE]), :, L % PAGE:, :] = value
+            pool[int(pt[b, L // PAGE]), :, L % PAGE:] = value
 
 
 @dataclasses.dataclass
@@ -197,6 +198,8 @@ def make_problem(name: str, seed: int = 0, device="cpu", layers: Optional[int] =
             if poison:
                 poison_dead_slots(k, L, pt, 0x7F)
                 poison_dead_slots(v, L, pt, 0x7F)
+                poison_dead_slots(kscale, L, pt, float("nan"))
+                poison_dead_slots(vscale, L, pt, float("nan"))
             ks.append(k)
             vs.append(v)
             kss.append(kscale)
