@@ -977,16 +977,26 @@ struct SharedLds {
 };
 
 // The tile as 16-byte chunks: K rows (chunk j < NK), V rows, then for fp8
-// the k and v scales (16 chunks each).  Thread t of T moves chunks
-// t, t + T, ...
+// the 16 chunks of k scales at 2 NK and the 16 of v scales at 2 NK + 64.
+// Thread t of T moves chunks t, t + T, ...  NK and T are multiples of 64,
+// so a wave's 64 chunks of a round are all K, all V, or one kind of scale:
+// the choice of source is wave-uniform.
 template <class KV, int D, int NCB>
 struct Staged {
     static constexpr int T = 64 * NCB;
     static constexpr int NK = kTile * KV::kRowBytes / 16;
-    static constexpr int NT = 2 * NK + (KV::kScaled ? 32 : 0);
+    static constexpr int KSC = 2 * NK, VSC = 2 * NK + 64;   // first scale chunks
+    static constexpr int NT = KV::kScaled ? VSC + 16 : 2 * NK;
     static constexpr int NCH = (NT + T - 1) / T;
+    static_assert(NK % 64 == 0, "K and V rounds split at wave boundaries");
     u32x4 c[NCH];
 };
+
+// The first chunk of this wave in round i (wave-uniform).
+template <class S>
+__device__ __forceinline__ int wave_chunk0(int i) {
+    return S::T * i + 64 * __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 
 template <class KV, int D, int NCB>
 __device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int h, int nv,
@@ -995,11 +1005,7 @@ __device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int 
     // Dead rows (token >= nv) and their scales read as zero.
     const auto kr = live_rows(p.k, page, h, p.Hkv, KV::kRowBytes, nv);
     const auto vr = live_rows(p.v, page, h, p.Hkv, KV::kRowBytes, nv);
-    __amdgpu_buffer_rsrc_t ksr = kr, vsr = vr;
-    if constexpr (KV::kScaled) {
-        ksr = live_rows(p.k_scale, page, h, p.Hkv, 4, nv);
-        vsr = live_rows(p.v_scale, page, h, p.Hkv, 4, nv);
-    }
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
         const int j = threadIdx.x + S::T * i;
@@ -1007,20 +1013,18 @@ __device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int 
             st.c[i] = ldb4(kr, 16 * j);
         } else if (S::T * i >= S::NK && S::T * (i + 1) <= 2 * S::NK) {   // all V
             st.c[i] = ldb4(vr, 16 * (j - S::NK));
-        } else if (j < S::NT) {
-            // A round across K, V and the scales: a lane's chunk comes from
-            // one of them, and the loads from the others are given an offset
-            // past any tile (they read 0 and touch no memory), so that no
-            // resource depends on the lane.
-            constexpr uint32_t kOut = 1u << 20;
-            const auto pick = [&](bool mine, int chunk) { return mine ? 16u * chunk : kOut; };
-            u32x4 x = ldb4(kr, pick(j < S::NK, j)) |
-                      ldb4(vr, pick(j >= S::NK && j < 2 * S::NK, j - S::NK));
-            if constexpr (KV::kScaled) {
-                const int q = j - 2 * S::NK;
-                x |= ldb4(ksr, pick(q >= 0 && q < 16, q)) | ldb4(vsr, pick(q >= 16, q - 16));
+        } else {   // a round across K, V and the scales: one source per wave
+            const int j0 = wave_chunk0<S>(i);
+            if (j0 < S::NK) {
+                st.c[i] = ldb4(kr, 16 * j);
+            } else if (j0 < 2 * S::NK) {
+                st.c[i] = ldb4(vr, 16 * (j - S::NK));
+            } else if constexpr (KV::kScaled) {
+                if (j0 == S::KSC && lane < 16)
+                    st.c[i] = ldb4(live_rows(p.k_scale, page, h, p.Hkv, 4, nv), 16 * lane);
+                else if (j0 == S::VSC && lane < 16)
+                    st.c[i] = ldb4(live_rows(p.v_scale, page, h, p.Hkv, 4, nv), 16 * lane);
             }
-            st.c[i] = x;
         }
     }
 }
@@ -1041,9 +1045,10 @@ __device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<K
             *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
         } else if (j < 2 * S::NK) {
             *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
-        } else if (j < S::NT) {
-            const int q = j - 2 * S::NK;
-            *reinterpret_cast<u32x4 *>((q < 16 ? sm.ks : sm.vs) + 4 * (q & 15)) = st.c[i];
+        } else if (KV::kScaled && j >= S::KSC && j < S::KSC + 16) {
+            *reinterpret_cast<u32x4 *>(sm.ks + 4 * (j - S::KSC)) = st.c[i];
+        } else if (KV::kScaled && j >= S::VSC && j < S::VSC + 16) {
+            *reinterpret_cast<u32x4 *>(sm.vs + 4 * (j - S::VSC)) = st.c[i];
         }
     }
 }
