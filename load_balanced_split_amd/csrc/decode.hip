@@ -159,6 +159,47 @@ __device__ __forceinline__ int sload(const int32_t *base, int64_t i) {
 }
 
 // ---------------------------------------------------------------------------
+// K rows through LDS.  The QK^T operand wants token r of a 16-token block in
+// lane r + 16 grp, 16 bytes of it per lane (MFMA rows are lanes mod 16).
+// Loaded in that shape straight from HBM, every load instruction takes one
+// 64-byte piece of each of 16 token rows, and such loads stream about 15%
+// (256-byte bf16 rows) to 20% (128-byte fp8 rows) slower than loads of
+// whole rows.  So K is loaded in whole rows (load c, lane l: bytes
+// 1024 c + 16 l of the wave's 16 rows) and each wave passes it through 16
+// rows of its own LDS, padded to CPR + 1 chunks of 16 bytes (CPR chunks per
+// row): the 16 lanes of a quarter-wave reading one chunk of 16 rows hit 16
+// distinct bank groups, and every address is a per-lane base plus a
+// constant.  The same wave stores and reads, and a wave's LDS operations run
+// in order, so no barrier is needed.
+// ---------------------------------------------------------------------------
+
+// Bytes of a wave's padded K rows.
+template <int CPR>
+constexpr int k_rows_bytes() {
+    return 16 * (CPR + 1) * 16;
+}
+
+// In: k[c] = bytes 1024 c + 16 lane of the wave's rows.  Out: k[c] = chunk
+// 4 c + grp of token r (the operand of k-step c, or of k-steps 2c, 2c+1 for
+// fp8).
+template <int CPR>
+__device__ __forceinline__ void k_to_operand(uint8_t *rows, int lane, int r, int grp,
+                                             u32x4 (&k)[CPR / 4]) {
+    constexpr int S = CPR + 1;   // padded row stride in chunks
+    uint8_t *wr = rows + 16 * (S * (lane / CPR) + lane % CPR);
+#pragma unroll
+    for (int c = 0; c < CPR / 4; ++c)
+        *reinterpret_cast<u32x4 *>(wr + 16 * S * (64 / CPR) * c) = k[c];
+    // other lanes' stores above, this lane's loads below: keep the order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint8_t *rd = rows + 16 * (S * r + grp);
+#pragma unroll
+    for (int c = 0; c < CPR / 4; ++c) k[c] = *reinterpret_cast<const u32x4 *>(rd + 64 * c);
+}
+
+// ---------------------------------------------------------------------------
 // Element formats.  Each provides the per-lane register image of one tile's
 // share of K and V, of the descriptor's Q, and the two MFMA operand builders.
 // ---------------------------------------------------------------------------
@@ -178,6 +219,10 @@ struct Bf16 {
 
     static constexpr int kQRowBytes = D * 2;
 
+    // K is loaded in the operand shape: no LDS rows.
+    static constexpr bool kKRows = false;
+    __device__ static void k_operand(uint8_t *, const Lane &, Tile &) {}
+
     // The MFMA B-operand image of Q (head g = r, d-range of k-step ks and
     // lane group grp) from the LDS copy of the group's rows.
     __device__ static void read_q(const uint32_t *sq, int stride, const Lane &ln, Q &q) {
@@ -192,6 +237,8 @@ struct Bf16 {
                                      const Lane &ln, Tile &t) {
         const auto kr = live_rows(p.k, page, h, p.Hkv, D * 2, nv);
         const auto vr = live_rows(p.v, page, h, p.Hkv, D * 2, nv);
+        // K straight in the operand shape: the 256-byte rows lose less to
+        // the piecewise row reads than the LDS round trip costs.
         const uint32_t koff = lane_off(((16 * ln.w + ln.r) * D + 8 * ln.grp) * 2);
         const uint32_t voff = lane_off(((16 * ln.w + 4 * ln.grp) * D + ln.r * (D / 16)) * 2);
 #pragma unroll
@@ -300,6 +347,12 @@ struct Fp8 {
 
     static constexpr int kQRowBytes = D;
 
+    // K is loaded in whole rows and reordered through the wave's LDS rows.
+    static constexpr bool kKRows = true;
+    __device__ static void k_operand(uint8_t *rows, const Lane &ln, Tile &t) {
+        k_to_operand<D / 16>(rows, ln.lane, ln.r, ln.grp, t.k);
+    }
+
     __device__ static void read_q(const uint32_t *sq, int stride, const Lane &ln, Q &q) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -311,10 +364,11 @@ struct Fp8 {
                                      const Lane &ln, Tile &t) {
         const auto kr = live_rows(p.k, page, h, p.Hkv, D, nv);
         const auto vr = live_rows(p.v, page, h, p.Hkv, D, nv);
-        const uint32_t koff = lane_off((16 * ln.w + ln.r) * D + 16 * ln.grp);
+        // K in whole rows (k_to_operand reorders them through LDS)
+        const uint32_t koff = lane_off(16 * ln.w * D + 16 * ln.lane);
         const uint32_t voff = lane_off((16 * ln.w + 4 * ln.grp) * D + ln.r * (D / 16));
 #pragma unroll
-        for (int c = 0; c < NC; ++c) t.k[c] = ldb4(kr, koff + 64 * c);
+        for (int c = 0; c < NC; ++c) t.k[c] = ldb4(kr, koff + 1024 * c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t off = voff + j * D;
@@ -521,23 +575,43 @@ __device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_
 
 // LDS scratch for merging the 4 waves of a workgroup, one 16-column block
 // at a time (GR = 8 when a workgroup has at most 8 columns).
-template <int D, int GR, int NCB>
+template <int D, int GR, int NCB, int QW>
 struct MergeLds {
     float o[kWaves][GR][D];
     float m[kWaves][GR];
     float l[kWaves][GR];
-    // The current descriptor's Q rows (16 NCB rows, rows >= R G zero), each
-    // padded by 4 dwords so that the per-tile operand reads are bank-conflict
-    // free.
-    uint32_t q[16 * NCB * (D / 2 + 4)];
+    // The current descriptor's Q rows of QW words (16 NCB rows, rows >= R G
+    // zero), each padded by 4 dwords so that the per-tile operand reads are
+    // bank-conflict free.
+    uint32_t q[16 * NCB * (QW + 4)];
     int last;   // the fused combine: this workgroup merges the segment
 };
+
+// Each wave's 16 padded K rows of RB bytes, on their way to the QK^T
+// operand.
+template <int RB, bool On = true>
+struct KRows {
+    alignas(16) uint8_t rows[kWaves][k_rows_bytes<RB / 16>()];
+};
+template <int RB>
+struct KRows<RB, false> {
+    uint8_t unused;
+};
+
+// This wave's K rows (nullptr where the format needs none).
+template <int RB, bool On>
+__device__ __forceinline__ uint8_t *k_rows_of(KRows<RB, On> &kr) {
+    if constexpr (On)
+        return kr.rows[threadIdx.x >> 6];
+    else
+        return nullptr;
+}
 
 // Copy the R G query rows of (b, h) into the LDS Q rows: LDS row r G + g is
 // query row r, head h G + g (the G heads of one row are contiguous in q).
 // All threads.
-template <class KV, int D, int GR, int NCB, bool MR>
-__device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR, NCB> &sm, int b,
+template <class KV, int D, int GR, int NCB, bool MR, int QW>
+__device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR, NCB, QW> &sm, int b,
                                         int h) {
     constexpr int RW = KV::kQRowBytes / 4, QS = RW + 4;
     const int R = rows_per_req<MR>(p);
@@ -694,9 +768,9 @@ __device__ __forceinline__ int seg_chunks(const DecodeParams &p, int b, int h, i
 
 // Merge the waves' states and write partial slot `slot` (R G rows).  All
 // threads.
-template <int D, int GR, int NCB, bool MR, bool FU, class Between>
+template <int D, int GR, int NCB, bool MR, bool FU, class Between, int QW>
 __device__ __forceinline__ void merge_write(const DecodeParams &p, State<D, NCB> &st,
-                                            MergeLds<D, GR, NCB> &sm, int64_t slot, int b, int h,
+                                            MergeLds<D, GR, NCB, QW> &sm, int64_t slot, int b, int h,
                                             const Lane &ln, Between between) {
     const int RG = rows_per_req<MR>(p) * p.G;
     int64_t k0;
@@ -887,10 +961,10 @@ struct Fairness {
 // i + 1 (across descriptor boundaries) is being loaded into the other
 // register buffer.  The run starts at `first` and ends with descriptor
 // d_end - 1; partials go to slot d (by_desc) or to slot_base.
-template <class KV, int D, int GR, int NCB, bool MR, bool FU>
-__device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB> &sm,
-                                      const MapSource &src, const Pos &first, int d_end,
-                                      int64_t slot_base, bool by_desc) {
+template <class KV, int D, int GR, int NCB, bool MR, bool FU, int QW>
+__device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB, QW> &sm,
+                                      uint8_t *krows, const MapSource &src, const Pos &first,
+                                      int d_end, int64_t slot_base, bool by_desc) {
     using Tile = typename KV::Tile;
     const Lane ln;
     const Cols<NCB> cols = columns<NCB, MR>(p, ln);
@@ -899,7 +973,7 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
     int nv_cur;
 
     // Q rows past R G stay zero for the whole kernel.
-    for (int i = threadIdx.x; i < 16 * NCB * (D / 2 + 4); i += kDecodeThreads) sm.q[i] = 0u;
+    for (int i = threadIdx.x; i < (int)(sizeof(sm.q) / 4); i += kDecodeThreads) sm.q[i] = 0u;
     __syncthreads();
     stage_q<KV, D, GR, NCB, MR>(p, sm, cur.b, cur.h);
     float qs[NCB];
@@ -926,6 +1000,7 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
         KV::load_tile(p, pg_n, far.h, more ? nv_n : 0, ln, nxt);
 
         if (by_desc) fair.tile();
+        KV::k_operand(krows, ln, now);
         attend_tile<KV, D, NCB, MR>(p, sm.q, qs, now, nv_cur, cols, st, ln);
 
         if (!more || n.d != cur.d) {
@@ -1252,14 +1327,15 @@ template <class KV, int D, int GR, int NCB, bool MR, bool FU>
 __global__ void __launch_bounds__(kDecodeThreads)
 __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<NCB>)))
 decode_kernel(DecodeParams p) {
-    __shared__ MergeLds<D, GR, NCB> sm;
+    __shared__ MergeLds<D, GR, NCB, KV::kQRowBytes / 4> sm;
+    __shared__ KRows<KV::kQRowBytes, KV::kKRows> kr;
     if constexpr (FU) clear_empty_segments<D>(p, kDecodeThreads);
     const MapLayout lay(p.B, p.Hkv, p.P);
     const int32_t *bin_off = p.map + lay.bin_off;
     const int d0 = uniform(bin_off[blockIdx.x]), d1 = uniform(bin_off[blockIdx.x + 1]);
     if (d0 >= d1) return;
     const MapSource src{p.map + lay.desc, p.map + lay.lens};
-    drain<KV, D, GR, NCB, MR, FU>(p, sm, src, src.read(d0), d1, 0, true);
+    drain<KV, D, GR, NCB, MR, FU>(p, sm, k_rows_of(kr), src, src.read(d0), d1, 0, true);
 }
 
 // The static ablation keeps the compiler's register allocation (two
@@ -1268,7 +1344,8 @@ decode_kernel(DecodeParams p) {
 template <class KV, int D, int GR, int NCB, bool MR>
 __global__ void __launch_bounds__(kDecodeThreads)
 static_decode_kernel(DecodeParams p) {
-    __shared__ MergeLds<D, GR, NCB> sm;
+    __shared__ MergeLds<D, GR, NCB, KV::kQRowBytes / 4> sm;
+    __shared__ KRows<KV::kQRowBytes, KV::kKRows> kr;
     const int64_t slot = blockIdx.x;
     const int64_t seg = slot / p.splits;
     const int k = (int)(slot % p.splits);
@@ -1291,8 +1368,8 @@ static_decode_kernel(DecodeParams p) {
     }
     // The same drain as the dynamic kernel, over one range and no map: with
     // d_end = 1 and the range numbered 0 it never reads a descriptor.
-    drain<KV, D, GR, NCB, MR, false>(p, sm, MapSource{nullptr, nullptr},
-                              Pos{0, b, h, (int)t0, (int)t1, L}, 1, slot, false);
+    drain<KV, D, GR, NCB, MR, false>(p, sm, k_rows_of(kr), MapSource{nullptr, nullptr},
+                                     Pos{0, b, h, (int)t0, (int)t1, L}, 1, slot, false);
 }
 
 // Shared-tile kernels (2 .. 4 column blocks): NCB waves per workgroup,
