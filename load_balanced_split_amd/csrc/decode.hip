@@ -147,6 +147,12 @@ __device__ __forceinline__ uint32_t ldb1(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNontemporal);
 }
 
+// A 16-byte buffer load with the default (temporal) cache policy, for lines
+// that a second wave reads soon after the first.
+__device__ __forceinline__ u32x4 ldb4_keep(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
 // Wave-uniform by construction (same address for every lane): keep it in a
 // scalar register so tile bases use the scalar-base load form.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -380,10 +386,15 @@ struct Fp8 {
             }
         }
         // Scales of tokens 16 w + 4 grp + i: one 16-byte run per lane group
-        // (the bound is checked per dword).
+        // (the bound is checked per dword).  Waves 2 k and 2 k + 1 read the
+        // two halves of one 128-byte line, so these loads keep the default
+        // cache policy: with the streaming one the line was often fetched
+        // twice (1.5% more HBM reads, 3% more time).
         const uint32_t soff = lane_off((16 * ln.w + 4 * ln.grp) * 4);
-        t.ks = __builtin_bit_cast(f32x4, ldb4(live_rows(p.k_scale, page, h, p.Hkv, 4, nv), soff));
-        t.vs = __builtin_bit_cast(f32x4, ldb4(live_rows(p.v_scale, page, h, p.Hkv, 4, nv), soff));
+        t.ks = __builtin_bit_cast(f32x4,
+                                  ldb4_keep(live_rows(p.k_scale, page, h, p.Hkv, 4, nv), soff));
+        t.vs = __builtin_bit_cast(f32x4,
+                                  ldb4_keep(live_rows(p.v_scale, page, h, p.Hkv, 4, nv), soff));
     }
 
     __device__ static f32x4 scores(const DecodeParams &p, const Q &q, const Tile &t,
