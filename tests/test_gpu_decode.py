@@ -97,6 +97,23 @@ def test_fp8_small_parity(R, D):
         run_and_compare(R, prob, "fp8 D=%d P=%d" % (D, P), P=P, m=1)
 
 
+FP8_SHAPES = [  # (H_kv, G, D): one and two 8-row halves, odd groups, both head dims
+    (1, 1, 64), (1, 16, 128), (3, 3, 128), (2, 16, 64),
+]
+
+
+@pytest.mark.parametrize("Hkv,G,D", FP8_SHAPES)
+def test_fp8_shapes_and_ragged_lengths(R, Hkv, G, D):
+    """fp8 K goes through per-wave LDS rows (whole-row loads); these shapes
+    cover both row widths (64 and 128 bytes) and both merge widths."""
+    lens = np.array([0, 1, 63, 64, 65, 127, 1000, 2049, 7], np.int32)
+    for P, m in ((1, 1), (7, 3), (300, 2)):
+        prob = wl.make_problem("fp8", seed=P + D, device="cuda", lens=lens, poison=True,
+                               workload=custom_workload(Hkv, G, D, "fp8"))
+        run_and_compare(R, prob, "fp8 shape Hkv=%d G=%d D=%d P=%d m=%d" % (Hkv, G, D, P, m),
+                        P=P, m=m)
+
+
 def test_fp8_decodes_every_code_exactly(R):
     """One token per request, V = every finite e4m3 code, v_scale = 1: the
     output is that token's V, exactly representable in bf16."""
