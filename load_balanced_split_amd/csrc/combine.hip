@@ -18,11 +18,13 @@
 // A workgroup of 4 waves merges 4 / WPR rows of one segment, WPR waves per
 // row.  Wave k of a row merges chunks k, k + WPR, ... in one pass with a
 // running maximum (each lane owns D/64 consecutive elements of the row, so a
-// chunk's row is one coalesced read), four chunks' loads in flight per wave;
+// chunk's row is one coalesced read), U chunks' loads in flight per wave;
 // with WPR > 1 the row's waves are then merged in LDS.  WPR = 4 suits
-// segments cut into many chunks (a long request over many bins), WPR = 1
-// segments of a few chunks with many rows.  A chunk with lse = -inf (an
-// empty static split) carries no weight and its row is never read.
+// segments cut into many chunks (a long request over many bins; U = 16, so
+// 64 chunks take one round of loads), WPR = 1 segments of a few chunks with
+// many rows (U = 4).  A chunk with lse = -inf (an empty static split, whose
+// O row is never written) carries no weight: its row is loaded with the
+// others, so that no load waits for another, but never enters the sums.
 #include "common.h"
 
 namespace hpcattn {
@@ -30,8 +32,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 4;
 constexpr float kNegInf = -__builtin_inff();
+
+// Chunks in flight per wave.
+template <int WPR>
+constexpr int unroll() {
+    return WPR > 1 ? 16 : 4;
+}
 
 // Running log-sum-exp merge state of one wave lane: max M, weight sum W and
 // the weighted row `acc` (both relative to M).
@@ -72,21 +79,22 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(CombineParams p) {
     }
     const int64_t n = c < RG ? k1 - k0 : 0;   // rows past R G (last workgroup) merge nothing
 
+    constexpr int U = unroll<WPR>();
     Merge<E> mg;
-    for (int64_t k = part; k < n; k += WPR * kUnroll) {
-        float l[kUnroll];
-        float o[kUnroll][E];
+    for (int64_t k = part; k < n; k += WPR * U) {
+        float l[U];
+        float o[U][E];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {   // past n: row k again, with no weight
             const int64_t kk = k + u * WPR;
             const int64_t row = (k0 + (kk < n ? kk : k)) * RG + c;
             l[u] = kk < n ? p.part_lse[row] : kNegInf;
             const float *src = p.part_o + row * D + lane * E;
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[u][e] = l[u] == kNegInf ? 0.f : src[e];
+            for (int e = 0; e < E; ++e) o[u][e] = src[e];
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) mg.add(l[u], o[u]);
+        for (int u = 0; u < U; ++u) mg.add(l[u], o[u]);   // skips lse = -inf
     }
     if constexpr (WPR > 1) {
         if (lane == 0) {

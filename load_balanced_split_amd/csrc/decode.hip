@@ -21,9 +21,11 @@
 //     group (G heads, times R rows of a multi-row step, R G <= 16) as 16 MFMA
 //     columns: S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,fp8} (16 tokens x 16
 //     columns), O^T += V^T P^T on v_mfma_f32_16x16x16_bf16;
-//   * K and V go straight from HBM to registers with 16-byte loads: lane
-//     (r = lane % 16, grp = lane / 16) reads token 16 w + r of K at a d-range
-//     that only has to match Q's, and tokens 16 w + 4 grp + j of V at
+//   * K and V go from HBM to registers with 16-byte loads: lane
+//     (r = lane % 16, grp = lane / 16) holds token 16 w + r of K at a
+//     d-range that only has to match Q's (bf16: loaded in that shape; fp8:
+//     loaded in whole rows and reordered through the wave's LDS rows, see
+//     "K rows through LDS"), and tokens 16 w + 4 grp + j of V at
 //     d = r * D/16 .. + D/16, repacked to the MFMA operand with v_perm;
 //     these are nontemporal buffer loads (every KV byte is read once)
 //     bounded at the tile's live rows, so dead rows read as zero and cost
