@@ -172,13 +172,14 @@ __device__ __forceinline__ int sload(const int32_t *base, int64_t i) {
 // Loaded in that shape straight from HBM, every load instruction takes one
 // 64-byte piece of each of 16 token rows, and such loads stream about 15%
 // (256-byte bf16 rows) to 20% (128-byte fp8 rows) slower than loads of
-// whole rows.  So K is loaded in whole rows (load c, lane l: bytes
+// whole rows.  So fp8 K is loaded in whole rows (load c, lane l: bytes
 // 1024 c + 16 l of the wave's 16 rows) and each wave passes it through 16
 // rows of its own LDS, padded to CPR + 1 chunks of 16 bytes (CPR chunks per
 // row): the 16 lanes of a quarter-wave reading one chunk of 16 rows hit 16
 // distinct bank groups, and every address is a per-lane base plus a
 // constant.  The same wave stores and reads, and a wave's LDS operations run
-// in order, so no barrier is needed.
+// in order, so no barrier is needed.  bf16 K keeps the operand-shaped loads:
+// on its wider rows the loss is smaller than the cost of the round trip.
 // ---------------------------------------------------------------------------
 
 // Bytes of a wave's padded K rows.
