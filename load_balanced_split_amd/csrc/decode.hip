@@ -492,11 +492,25 @@ struct Fp8 {
 // Per-wave online-softmax state and the 4-wave merge.
 // ---------------------------------------------------------------------------
 
+// A column of the S^T / O^T tiles is held by lanes r, r + 16, r + 32 and
+// r + 48 (4 token groups): its max and sum across them.  All lanes.
+__device__ __forceinline__ float column_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float column_sum(float x) {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+}
+
 template <int D, int NCB>
 struct State {
     static constexpr int NB = D / 16;   // 16-wide d-blocks of O^T
     f32x4 o[NCB][NB];   // O[column 16 cb + r][d = (4 grp + i) * D/16 + blk]
-    float m[NCB], l[NCB];   // running max (log2 units) and sum of that column
+    // Running max (log2 units) of the column, the same in its 4 lanes, and
+    // the running sum of the weights of this lane's tokens: the column's sum
+    // is column_sum(l) (the 4 lanes are rescaled by the same factors).
+    float m[NCB], l[NCB];
 
     __device__ void reset() {
 #pragma unroll
@@ -541,12 +555,13 @@ __device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_
                 if (tok0 + i >= lim) s[i] = kNegInf;
         }
         float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         // The reference max moves only when a tile's max exceeds it by more
         // than kSlack (log2 units), so weights stay <= 2^kSlack and O, l are
-        // rescaled (a wave-uniform branch) only on those rare tiles.
+        // rescaled (a wave-uniform branch) only on those rare tiles.  A
+        // column's max exceeds the bound iff one of its lanes' maxima does,
+        // so the column max is reduced across lanes only on that branch.
         if (__any(mx > st.m[cb] + kSlack)) {
+            mx = column_max(mx);
             const bool moves = mx > st.m[cb] + kSlack;
             const float m_new = moves ? mx : st.m[cb];
             // 1 where the reference is kept (also when it stays -inf), 0 from -inf
@@ -560,10 +575,7 @@ __device__ __forceinline__ void attend_tile(const DecodeParams &p, const uint32_
         f32x4 pr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-        float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        st.l[cb] += ps;
+        st.l[cb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);   // this lane's tokens only
 
         if constexpr (KV::kScaled) pr = pr * t.vs;   // fold the per-token V scale into P
         pb[cb] = __builtin_bit_cast(s16x4,
@@ -792,10 +804,11 @@ __device__ __forceinline__ void merge_write(const DecodeParams &p, State<D, NCB>
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int c0 = 16 * cb;
+        const float lsum = column_sum(st.l[cb]);
         if (c0 + ln.r < RG) {
             if (ln.grp == 0) {
                 sm.m[ln.w][ln.r] = st.m[cb];
-                sm.l[ln.w][ln.r] = st.l[cb];
+                sm.l[ln.w][ln.r] = lsum;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1177,9 +1190,8 @@ __device__ __forceinline__ void attend_shared(const DecodeParams &p, const Share
         }
         float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         if (__any(mx > st.m[0] + kSlack)) {   // stale reference max, as in attend_tile
+            mx = column_max(mx);
             const bool moves = mx > st.m[0] + kSlack;
             const float m_new = moves ? mx : st.m[0];
             const float alpha = moves ? __builtin_amdgcn_exp2f(st.m[0] - m_new) : 1.f;
@@ -1202,9 +1214,7 @@ __device__ __forceinline__ void attend_shared(const DecodeParams &p, const Share
             pw[2 * u] = pack_bf16(pr[0], pr[1]);
             pw[2 * u + 1] = pack_bf16(pr[2], pr[3]);
         }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        st.l[0] += ps;
+        st.l[0] += ps;   // this lane's tokens only
 
         // O^T += V^T P^T over the half's 32 tokens: k-slot e < 4 of k-group
         // g is token 32 th + 4 g + e, e >= 4 token 32 th + 16 + 4 g + e - 4
@@ -1226,9 +1236,10 @@ __device__ __forceinline__ void write_columns(const DecodeParams &p, const State
                                               int col0, int64_t slot, const Lane &ln) {
     const int RG = p.R * p.G;
     const int col = col0 + ln.r;
+    const float l = column_sum(st.l[0]);
     if (col >= RG) return;
-    const bool live = st.l[0] > 0.f;
-    const float inv = live ? 1.0f / st.l[0] : 0.f;
+    const bool live = l > 0.f;
+    const float inv = live ? 1.0f / l : 0.f;
     char *obase = reinterpret_cast<char *>(p.part_o + slot * RG * D);
     // accumulator blk holds d = 16 blk + 4 grp .. 16 blk + 4 grp + 3
 #pragma unroll
@@ -1236,7 +1247,7 @@ __device__ __forceinline__ void write_columns(const DecodeParams &p, const State
         *reinterpret_cast<f32x4 *>(obase + (uint32_t)(col * D + 16 * blk + 4 * ln.grp) * 4u) =
             st.o[0][blk] * inv;
     if (ln.grp == 0)
-        p.part_lse[slot * RG + col] = live ? (st.m[0] + log2f(st.l[0])) * kLn2 : kNegInf;
+        p.part_lse[slot * RG + col] = live ? (st.m[0] + log2f(l)) * kLn2 : kNegInf;
 }
 
 // This lane's column of the shared-tile path: its query row's lag, its
