@@ -1080,12 +1080,13 @@ struct SharedLds {
 
 // The tile as 16-byte chunks: K rows (chunk j < NK), V rows, then for fp8
 // the 16 chunks of k scales at 2 NK and the 16 of v scales at 2 NK + 64.
-// Thread t of T moves chunks t, t + T, ...  NK and T are multiples of 64,
+// Staging thread t of T (all threads of the workgroup, or the 64 of its
+// staging wave) moves chunks t, t + T, ...  NK and T are multiples of 64,
 // so a wave's 64 chunks of a round are all K, all V, or one kind of scale:
 // the choice of source is wave-uniform.
-template <class KV, int D, int NCB>
+template <class KV, int D, int T_>
 struct Staged {
-    static constexpr int T = 64 * NCB;
+    static constexpr int T = T_;
     static constexpr int NK = kTile * KV::kRowBytes / 16;
     static constexpr int KSC = 2 * NK, VSC = 2 * NK + 64;   // first scale chunks
     static constexpr int NT = KV::kScaled ? VSC + 16 : 2 * NK;
@@ -1094,29 +1095,29 @@ struct Staged {
     u32x4 c[NCH];
 };
 
-// The first chunk of this wave in round i (wave-uniform).
+// The first chunk of staging thread tid's wave in round i (wave-uniform).
 template <class S>
-__device__ __forceinline__ int wave_chunk0(int i) {
-    return S::T * i + 64 * __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+__device__ __forceinline__ int wave_chunk0(int i, int tid) {
+    return S::T * i + 64 * __builtin_amdgcn_readfirstlane(tid >> 6);
 }
 
-template <class KV, int D, int NCB>
+template <class KV, int D, int T>
 __device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int h, int nv,
-                                           Staged<KV, D, NCB> &st) {
-    using S = Staged<KV, D, NCB>;
+                                           Staged<KV, D, T> &st, int tid) {
+    using S = Staged<KV, D, T>;
     // Dead rows (token >= nv) and their scales read as zero.
     const auto kr = live_rows(p.k, page, h, p.Hkv, KV::kRowBytes, nv);
     const auto vr = live_rows(p.v, page, h, p.Hkv, KV::kRowBytes, nv);
-    const int lane = threadIdx.x & 63;
+    const int lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
-        const int j = threadIdx.x + S::T * i;
+        const int j = tid + S::T * i;
         if (S::T * (i + 1) <= S::NK) {   // all K (a whole round of chunks)
             st.c[i] = ldb4(kr, 16 * j);
         } else if (S::T * i >= S::NK && S::T * (i + 1) <= 2 * S::NK) {   // all V
             st.c[i] = ldb4(vr, 16 * (j - S::NK));
         } else {   // a round across K, V and the scales: one source per wave
-            const int j0 = wave_chunk0<S>(i);
+            const int j0 = wave_chunk0<S>(i, tid);
             if (j0 < S::NK) {
                 st.c[i] = ldb4(kr, 16 * j);
             } else if (j0 < 2 * S::NK) {
@@ -1134,15 +1135,16 @@ __device__ __forceinline__ void stage_load(const DecodeParams &p, int page, int 
 // K and V chunks go to row j / CPR, column j % CPR of the K-then-V rows
 // (CPR chunks per row); a round of T threads covers T / CPR whole rows, so
 // the address of round i is the thread's first address plus a constant.
-template <class KV, int D, int NCB>
-__device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, NCB> &st) {
-    using S = Staged<KV, D, NCB>;
+template <class KV, int D, int T>
+__device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, T> &st,
+                                            int tid) {
+    using S = Staged<KV, D, T>;
     constexpr int kRow = SharedLds<KV, D>::kRow, CPR = KV::kRowBytes / 16;
     static_assert(S::T % CPR == 0, "a round of chunks covers whole rows");
-    uint8_t *base = sm.kv + (threadIdx.x / CPR) * kRow + 16 * (threadIdx.x % CPR);
+    uint8_t *base = sm.kv + (tid / CPR) * kRow + 16 * (tid % CPR);
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
-        const int j = threadIdx.x + S::T * i;
+        const int j = tid + S::T * i;
         if (S::T * (i + 1) <= 2 * S::NK) {   // a whole round of K / V chunks
             *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
         } else if (j < 2 * S::NK) {
@@ -1301,15 +1303,16 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
     Pos cur = first;
     int nv_cur;
     Pos pre = read_ahead(src, d_end, cur);
-    Staged<KV, D, NCB> stg;
+    Staged<KV, D, 64 * NCB> stg;
+    const int tid = threadIdx.x;
     {
         const int pg = locate(p, cur, nv_cur);
-        stage_load<KV, D, NCB>(p, pg, cur.h, nv_cur, stg);
+        stage_load<KV, D, 64 * NCB>(p, pg, cur.h, nv_cur, stg, tid);
     }
     load_q_direct<KV>(p, cur, col, ln, q);
     float qs = q_scale_at(cur);
     st.reset();
-    stage_store<KV, D, NCB>(sm, stg);
+    stage_store<KV, D, 64 * NCB>(sm, stg, tid);
     __syncthreads();
     // The dynamic kernel's bins hold q tiles each (header word 2 of the map).
     Fairness fair(by_desc ? sload(p.map, 2) : 1 << 30);
@@ -1321,7 +1324,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         const Pos far = pick(more, n, cur);
         int nv_n;
         const int pg_n = locate(p, far, nv_n);
-        stage_load<KV, D, NCB>(p, pg_n, far.h, more ? nv_n : 0, stg);
+        stage_load<KV, D, 64 * NCB>(p, pg_n, far.h, more ? nv_n : 0, stg, tid);
 
         if (by_desc) fair.tile();
         attend_shared<KV, D>(p, sm, q, qs, nv_cur, col.lag, st, ln);
@@ -1335,7 +1338,86 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
             qs = q_scale_at(n);
             st.reset();
         }
-        stage_store<KV, D, NCB>(sm, stg);
+        stage_store<KV, D, 64 * NCB>(sm, stg, tid);
+        __syncthreads();   // tile t + 1 is in LDS
+        cur = n;
+        nv_cur = nv_n;
+    }
+}
+
+// The same walk with a staging wave: waves 0 .. NCB - 1 compute from LDS
+// and wave NCB alone copies tile t + 1 HBM -> registers -> LDS.  Nothing
+// that one kind of wave holds is live in the other's loop, so the staging
+// wave's 2 NK / 64 chunks per lane and the compute waves' accumulators do
+// not add up.  Both loops take the same barriers: one when the tile in LDS
+// is no longer read, one when the next tile is in.
+template <class KV, int D, int NCB>
+__device__ __forceinline__ void drain_shared_staged(const DecodeParams &p, SharedLds<KV, D> &sm,
+                                                    const MapSource &src, const Pos &first,
+                                                    int d_end, int64_t slot_base, bool by_desc) {
+    const Lane ln;
+    Pos cur = first;
+    Pos pre = read_ahead(src, d_end, cur);
+    if (uniform(ln.w) == NCB) {
+        __builtin_amdgcn_s_setprio(3);   // its loads and stores go first
+        Staged<KV, D, 64> stg;
+        int nv;
+        const int pg = locate(p, cur, nv);
+        stage_load<KV, D, 64>(p, pg, cur.h, nv, stg, ln.lane);
+        stage_store<KV, D, 64>(sm, stg, ln.lane);
+        __syncthreads();
+        while (true) {
+            Pos n;
+            const bool more = advance_ahead(d_end, cur, pre, n);
+            const Pos far = pick(more, n, cur);
+            int nv_n;
+            const int pg_n = locate(p, far, nv_n);
+            stage_load<KV, D, 64>(p, pg_n, far.h, more ? nv_n : 0, stg, ln.lane);
+            __syncthreads();   // every compute wave is done with the tile in LDS
+            if (!more) return;
+            if (n.d != cur.d) pre = read_ahead(src, d_end, n);
+            stage_store<KV, D, 64>(sm, stg, ln.lane);
+            __syncthreads();   // tile t + 1 is in LDS
+            cur = n;
+        }
+    }
+
+    const SharedCol col(p, ln);
+    auto q_scale_at = [&](const Pos &x) __attribute__((always_inline)) -> float {
+        if constexpr (KV::kScaled)
+            return ldg<float>(p.q_scale + ((int64_t)x.b * p.R * p.Hq + (int64_t)x.h * p.G),
+                              (uint32_t)col.qoff * 4u);
+        else
+            return 1.f;
+    };
+    State<D, 1> st;
+    typename KV::Q q;
+    int nv_cur;
+    locate(p, cur, nv_cur);
+    load_q_direct<KV>(p, cur, col, ln, q);
+    float qs = q_scale_at(cur);
+    st.reset();
+    __syncthreads();   // the first tile is in LDS
+    Fairness fair(by_desc ? sload(p.map, 2) : 1 << 30);
+    if (by_desc) fair.start();
+
+    while (true) {
+        Pos n;
+        const bool more = advance_ahead(d_end, cur, pre, n);
+        int nv_n;
+        locate(p, pick(more, n, cur), nv_n);
+        if (by_desc) fair.tile();
+        attend_shared<KV, D>(p, sm, q, qs, nv_cur, col.lag, st, ln);
+        __syncthreads();   // done with the tile in LDS
+
+        if (!more || n.d != cur.d) {
+            write_columns<D>(p, st, 16 * ln.w, by_desc ? (int64_t)cur.d : slot_base, ln);
+            if (!more) return;
+            pre = read_ahead(src, d_end, n);
+            load_q_direct<KV>(p, n, col, ln, q);
+            qs = q_scale_at(n);
+            st.reset();
+        }
         __syncthreads();   // tile t + 1 is in LDS
         cur = n;
         nv_cur = nv_n;
@@ -1397,10 +1479,10 @@ static_decode_kernel(DecodeParams p) {
                                      Pos{0, b, h, (int)t0, (int)t1, L}, 1, slot, false);
 }
 
-// Shared-tile kernels (2 .. 4 column blocks): NCB waves per workgroup,
-// sized for three waves per SIMD.
-template <class KV, int D, int NCB>
-__global__ void __launch_bounds__(64 * NCB) __attribute__((amdgpu_waves_per_eu(3)))
+// Shared-tile kernels (2 .. 4 column blocks): NCB compute waves per
+// workgroup, plus a staging wave when SW, sized for three waves per SIMD.
+template <class KV, int D, int NCB, int SW>
+__global__ void __launch_bounds__(64 * (NCB + SW)) __attribute__((amdgpu_waves_per_eu(3)))
 decode_shared_kernel(DecodeParams p) {
     __shared__ SharedLds<KV, D> sm;
     const MapLayout lay(p.B, p.Hkv, p.P);
@@ -1408,11 +1490,14 @@ decode_shared_kernel(DecodeParams p) {
     const int d0 = uniform(bin_off[blockIdx.x]), d1 = uniform(bin_off[blockIdx.x + 1]);
     if (d0 >= d1) return;
     const MapSource src{p.map + lay.desc, p.map + lay.lens};
-    drain_shared<KV, D, NCB>(p, sm, src, src.read(d0), d1, 0, true);
+    if constexpr (SW)
+        drain_shared_staged<KV, D, NCB>(p, sm, src, src.read(d0), d1, 0, true);
+    else
+        drain_shared<KV, D, NCB>(p, sm, src, src.read(d0), d1, 0, true);
 }
 
-template <class KV, int D, int NCB>
-__global__ void __launch_bounds__(64 * NCB) static_decode_shared_kernel(DecodeParams p) {
+template <class KV, int D, int NCB, int SW>
+__global__ void __launch_bounds__(64 * (NCB + SW)) static_decode_shared_kernel(DecodeParams p) {
     __shared__ SharedLds<KV, D> sm;
     const int64_t slot = blockIdx.x;
     const int64_t seg = slot / p.splits;
@@ -1431,23 +1516,34 @@ __global__ void __launch_bounds__(64 * NCB) static_decode_shared_kernel(DecodePa
     }
     if (t0 >= t1) {   // an empty split: no weight in the combine
         const int RG = p.R * p.G;
-        for (int i = threadIdx.x; i < RG; i += 64 * NCB) p.part_lse[slot * RG + i] = kNegInf;
+        for (int i = threadIdx.x; i < RG; i += 64 * (NCB + SW))
+            p.part_lse[slot * RG + i] = kNegInf;
         return;
     }
-    drain_shared<KV, D, NCB>(p, sm, MapSource{nullptr, nullptr},
-                             Pos{0, b, h, (int)t0, (int)t1, L}, 1, slot, false);
+    const Pos range{0, b, h, (int)t0, (int)t1, L};
+    if constexpr (SW)
+        drain_shared_staged<KV, D, NCB>(p, sm, MapSource{nullptr, nullptr}, range, 1, slot, false);
+    else
+        drain_shared<KV, D, NCB>(p, sm, MapSource{nullptr, nullptr}, range, 1, slot, false);
 }
 
 // Column blocks of a workgroup: ceil(R G / 16), 1 .. 4.
 int column_blocks(int rows) { return (rows + 15) / 16; }
 
-// Waves of the shared-tile workgroup for NCB column blocks.  bf16 rows of
-// D = 128 at three waves would stage 11 chunks (44 registers) per thread,
-// beyond the 168 registers of three waves per SIMD; the spill waits for
-// every load each tile.  That case runs four waves, the fourth block padding.
+// Whether the shared-tile workgroup for NCB column blocks has a staging
+// wave (three column blocks at D = 128).  Each workgroup keeps one tile in
+// flight, so the bytes in flight per CU grow with the workgroups it holds.
+//   * bf16: three waves would stage 11 chunks (44 registers) per thread,
+//     beyond the 168 registers of three waves per SIMD (a spill waits for
+//     every load each tile).  A fourth wave holds the 32 chunks per lane
+//     instead, next to no accumulators: three workgroups per CU.
+//   * fp8: without staging registers the compute waves fit 128 registers,
+//     four waves per SIMD, so a CU holds four 4-wave workgroups where it
+//     held three 3-wave ones (draft verification, 6 rows of 8 heads:
+//     decode 430 -> 364 us).
 template <class KV, int D>
-constexpr int shared_waves(int ncb) {
-    return (ncb == 3 && !KV::kScaled && D == 128) ? 4 : ncb;
+constexpr int staging_wave(int ncb) {
+    return (ncb == 3 && D == 128) ? 1 : 0;
 }
 
 // Workgroups of three waves are held below what their registers allow, by
@@ -1460,14 +1556,14 @@ constexpr int shared_waves(int ncb) {
 // four at four.  Computed once per instance from its register count.
 constexpr int kLdsPerCu = 160 * 1024;
 
-template <class KV, int D, int NCB>
+template <class KV, int D, int NCB, int SW>
 unsigned shared_lds_pad() {
-    if constexpr (NCB != 3) {
+    if constexpr (NCB + SW != 3) {
         return 0u;
     } else {
         static const unsigned pad = [] {
             hipFuncAttributes a{};
-            if (hipFuncGetAttributes(&a, (const void *)decode_shared_kernel<KV, D, 3>) !=
+            if (hipFuncGetAttributes(&a, (const void *)decode_shared_kernel<KV, D, NCB, SW>) !=
                 hipSuccess)
                 return 0u;
             const int regs = (max(a.numRegs, 1) + 7) / 8 * 8;   // allocation granule
@@ -1482,12 +1578,13 @@ unsigned shared_lds_pad() {
 
 template <class KV, int D, int NCB>
 hipError_t launch_shared(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
+    constexpr int SW = staging_wave<KV, D>(NCB);
     if (dynamic)   // (the fused combine is not offered for these workgroups)
-        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB),
-                           (shared_lds_pad<KV, D, NCB>()), stream, p);
+        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB, SW>), dim3(grid),
+                           dim3(64 * (NCB + SW)), (shared_lds_pad<KV, D, NCB, SW>()), stream, p);
     else
-        hipLaunchKernelGGL((static_decode_shared_kernel<KV, D, NCB>), dim3(grid), dim3(64 * NCB),
-                           0, stream, p);
+        hipLaunchKernelGGL((static_decode_shared_kernel<KV, D, NCB, SW>), dim3(grid),
+                           dim3(64 * (NCB + SW)), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1519,7 +1616,7 @@ hipError_t launch_for(const DecodeParams &p, hipStream_t stream, bool dynamic, i
         return rows <= 8 ? launch_one<KV<D>, D, 8, 1, true>(p, stream, dynamic, grid)
                          : launch_one<KV<D>, D, 16, 1, true>(p, stream, dynamic, grid);
     case 2: return launch_shared<KV<D>, D, 2>(p, stream, dynamic, grid);
-    case 3: return launch_shared<KV<D>, D, shared_waves<KV<D>, D>(3)>(p, stream, dynamic, grid);
+    case 3: return launch_shared<KV<D>, D, 3>(p, stream, dynamic, grid);
     default: return launch_shared<KV<D>, D, 4>(p, stream, dynamic, grid);
     }
 }
@@ -1538,16 +1635,18 @@ hipError_t dispatch(const DecodeParams &p, int head_dim, int kv_dtype, hipStream
 // rows <= 16 (the resident count does not depend on R otherwise).
 template <template <int> class KV, int D>
 const void *decode_fn(int rows, int &threads, unsigned &lds_pad) {
+    constexpr int SW2 = staging_wave<KV<D>, D>(2), SW3 = staging_wave<KV<D>, D>(3),
+                  SW4 = staging_wave<KV<D>, D>(4);
     const int ncb = column_blocks(rows);
-    threads = ncb == 1 ? kDecodeThreads : 64 * shared_waves<KV<D>, D>(ncb);
-    lds_pad = ncb == 3 ? shared_lds_pad<KV<D>, D, shared_waves<KV<D>, D>(3)>() : 0u;
-    switch (column_blocks(rows)) {
+    threads = ncb == 1 ? kDecodeThreads : 64 * (ncb + staging_wave<KV<D>, D>(ncb));
+    lds_pad = ncb == 3 ? shared_lds_pad<KV<D>, D, 3, SW3>() : 0u;
+    switch (ncb) {
     case 1:
         return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false, false>
                          : (const void *)decode_kernel<KV<D>, D, 16, 1, false, false>;
-    case 2: return (const void *)decode_shared_kernel<KV<D>, D, 2>;
-    case 3: return (const void *)decode_shared_kernel<KV<D>, D, shared_waves<KV<D>, D>(3)>;
-    default: return (const void *)decode_shared_kernel<KV<D>, D, 4>;
+    case 2: return (const void *)decode_shared_kernel<KV<D>, D, 2, SW2>;
+    case 3: return (const void *)decode_shared_kernel<KV<D>, D, 3, SW3>;
+    default: return (const void *)decode_shared_kernel<KV<D>, D, 4, SW4>;
     }
 }
 
