@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import statistics
@@ -33,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn µs/step + KV-read GB/s (% HBM peak), mixed-length GQA batch"
 HBM_PEAK_GBS = 8000.0
+WARM_GPU_MS = 100.0   # least GPU time of untimed graph replays before the timed steps
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "load_balanced_split_amd", "csrc", "decode.hip")
 
@@ -402,7 +404,12 @@ def main():
     # synchronisation between them (as a serving loop enqueues its steps),
     # bracketed by a synchronize on each side.  Graph mode replays a graph of
     # `per_graph` consecutive steps, so that the one-layer workloads still
-    # rotate over their pools, and a one-step graph for any remainder.
+    # rotate over their pools, and a one-step graph for any remainder.  The
+    # captured graph first runs W untimed steps of its own, right before the
+    # timed region, for W steps and at least WARM_GPU_MS of GPU time: a GPU
+    # left idle by the capture needs some milliseconds to return to its
+    # running speed (about 25 ms of work on the draft-verify fp8 workload,
+    # whose first 20 steps ran 15% slower than the next ones).
     # Events between replays give the spread of the per-step time.
     per_graph = 1 if layers >= pools else pools // layers
 
@@ -413,14 +420,22 @@ def main():
         else:
             full, rem = divmod(args.steps, per_graph)
             chunks = []
+            g = capture(lambda: [one_step(k) for k in range(per_graph)])
             if full:
-                g = capture(lambda: [one_step(k) for k in range(per_graph)])
-                g.replay()
                 chunks += [(g.replay, per_graph)] * full
             if rem:
                 g1 = capture(lambda: one_step(0))
                 g1.replay()
                 chunks += [(g1.replay, 1)] * rem
+            a, b = events()
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            b.synchronize()
+            per_replay_ms = max(a.elapsed_time(b), 1e-3)
+            for _ in range(max(-(-args.warmup // per_graph),
+                               math.ceil(WARM_GPU_MS / per_replay_ms))):
+                g.replay()
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(chunks) + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
