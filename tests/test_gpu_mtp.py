@@ -101,10 +101,11 @@ def test_multi_row_sharp_softmax(R):
     assert stats["rel_l2"] <= 2e-2
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("policy,param", [(0, 1), (0, 5), (1, 256), (1, 4096)])
-def test_multi_row_static(R, policy, param):
+def test_multi_row_static(R, policy, param, kv):
     lens = np.array([0, 3, 64, 70, 1000, 5000], np.int32)
-    w = workload(2, 8, 128, 6)
+    w = workload(2, 8, 128, 6, kv)
     prob = wl.make_problem("tiny", seed=param, device="cuda", lens=lens, poison=True,
                            workload=w)
     run = R.DecodeRunner(prob)
@@ -113,7 +114,7 @@ def test_multi_row_static(R, policy, param):
     ref_o, ref_l = oracle_attention(host_inputs(prob))
     pairs = [(b, h) for b in range(len(lens)) for h in range(2)]
     check(run.out, run.out_lse, ref_o, ref_l, pairs, w,
-          "static rows=6 policy=%d param=%d" % (policy, param))
+          "static %s rows=6 policy=%d param=%d" % (kv, policy, param))
 
 
 @pytest.mark.parametrize("name,npairs", [("mtp", 8), ("mtp_fp8", 5)])
