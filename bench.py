@@ -295,8 +295,8 @@ def traffic_from_profile(workload: str):
 def cpu_baseline(prob, budget_s: float):
     """The fp64 oracle, as it stands, on all host cores over a bounded sample
     of layer 0: whole (request, KV head) pairs in a seeded order, cycling
-    over the layer, until the time budget is spent.  Returns the KV GB/s it
-    sustained."""
+    over the layer, until the time budget is spent; then the same on one
+    thread for a third of the budget.  Returns the KV GB/s they sustained."""
     import numpy as np
 
     import oracle
@@ -312,25 +312,36 @@ def cpu_baseline(prob, budget_s: float):
     rng = np.random.default_rng(7)
     pairs = [(int(b), hh) for b in rng.permutation(len(prob.seq_lens))
              for hh in range(w.num_kv_heads)]
-    cores = oracle.max_threads()
-    done_tok, spent, i = 0, 0.0, 0
-    chunk = max(cores, 8)
-    while spent < budget_s:
-        sel = [pairs[(i + k) % len(pairs)] for k in range(chunk)]
-        t0 = time.perf_counter()
-        oracle.attention(h["q"], h["k_pages"], h["v_pages"], h["page_table"], h["seq_lens"],
-                         num_kv_heads=w.num_kv_heads, sm_scale=prob.sm_scale,
-                         q_scale=h.get("q_scale"), k_scale=h.get("k_scale"),
-                         v_scale=h.get("v_scale"), pairs=sel)
-        spent += time.perf_counter() - t0
-        done_tok += sum(int(prob.seq_lens[b]) for b, _ in sel)
-        i += len(sel)
     per_tok_head = wl.kv_bytes_per_token(w) // w.num_kv_heads
-    gbs = done_tok * per_tok_head / spent / 1e9
+
+    def sample(budget, chunk):
+        done_tok, spent, i = 0, 0.0, 0
+        while spent < budget:
+            sel = [pairs[(i + k) % len(pairs)] for k in range(chunk)]
+            t0 = time.perf_counter()
+            oracle.attention(h["q"], h["k_pages"], h["v_pages"], h["page_table"],
+                             h["seq_lens"], num_kv_heads=w.num_kv_heads,
+                             sm_scale=prob.sm_scale, q_scale=h.get("q_scale"),
+                             k_scale=h.get("k_scale"), v_scale=h.get("v_scale"), pairs=sel)
+            spent += time.perf_counter() - t0
+            done_tok += sum(int(prob.seq_lens[b]) for b, _ in sel)
+            i += len(sel)
+        return done_tok * per_tok_head / spent / 1e9, i, done_tok, spent
+
+    cores = oracle.max_threads()
+    gbs, n, tok, spent = sample(budget_s, max(cores, 8))
+    oracle.set_threads(1)
+    try:
+        gbs1, n1, tok1, spent1 = sample(budget_s / 3, 1)
+    finally:
+        oracle.set_threads(cores)
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": "layer 0 of the same workload, %d (request, KV head) attention tasks "
                       "(%.2f passes over the layer's %d pairs, %d KV tokens), %.1f s of fp64 "
-                      "C/OpenMP work" % (i, i / len(pairs), len(pairs), done_tok, spent)}
+                      "C/OpenMP work" % (n, n / len(pairs), len(pairs), tok, spent),
+            "single_thread": {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": "%d attention tasks, %d KV tokens, %.1f s"
+                                        % (n1, tok1, spent1)}}
 
 
 def main():
