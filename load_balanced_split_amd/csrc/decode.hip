@@ -283,6 +283,9 @@ struct Bf16 {
     // the lane's KC 16-byte K chunks (chunk i at byte 64 i + 16 grp of its
     // token's row: the d-range of k-step i).
     static constexpr int kRowBytes = D * 2;
+    // LDS V row padding: 288-byte rows put the 4 consecutive rows of a
+    // transpose read 8 banks apart (4 lanes x 8 bytes per row).
+    static constexpr int kVPad = 32;
     static constexpr int KC = D / 32;
     __device__ static f32x4 qk(const u32x4 (&k)[KC], const Q &q) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -419,6 +422,8 @@ struct Fp8 {
     // Shared-tile path: raw Q K^T of 16 tokens from the lane's KC 16-byte K
     // chunks (chunk c at byte 64 c + 16 grp: k-steps 2 c and 2 c + 1).
     static constexpr int kRowBytes = D;
+    // LDS V row padding, as for K rows.
+    static constexpr int kVPad = 16;
     static constexpr int KC = D / 64;
     __device__ static f32x4 qk(const u32x4 (&k)[KC], const Q &q) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1070,12 +1075,14 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
 
 template <class KV, int D>
 struct SharedLds {
-    static constexpr int kRow = KV::kRowBytes + 16;   // padded row
-    alignas(16) uint8_t kv[2 * kTile * kRow];   // K rows 0 .. 63, then V rows
+    static constexpr int kRow = KV::kRowBytes + 16;           // padded K row
+    static constexpr int kRowV = KV::kRowBytes + KV::kVPad;   // padded V row
+    alignas(16) uint8_t kv[kTile * (kRow + kRowV)];   // K rows 0 .. 63, then V rows
     alignas(16) float ks[kTile];   // fp8 k and v scales of the tile's tokens
     alignas(16) float vs[kTile];
     __device__ const uint8_t *k() const { return kv; }
     __device__ const uint8_t *v() const { return kv + kTile * kRow; }
+    __device__ uint8_t *v() { return kv + kTile * kRow; }
 };
 
 // The tile as 16-byte chunks: K rows (chunk j < NK), V rows, then for fp8
@@ -1139,16 +1146,23 @@ template <class KV, int D, int T>
 __device__ __forceinline__ void stage_store(SharedLds<KV, D> &sm, const Staged<KV, D, T> &st,
                                             int tid) {
     using S = Staged<KV, D, T>;
-    constexpr int kRow = SharedLds<KV, D>::kRow, CPR = KV::kRowBytes / 16;
+    using L = SharedLds<KV, D>;
+    constexpr int CPR = KV::kRowBytes / 16;
     static_assert(S::T % CPR == 0, "a round of chunks covers whole rows");
-    uint8_t *base = sm.kv + (tid / CPR) * kRow + 16 * (tid % CPR);
+    uint8_t *kbase = sm.kv + (tid / CPR) * L::kRow + 16 * (tid % CPR);
+    // V chunk of round i: row tid / CPR + (T / CPR) i - 64, column tid % CPR
+    uint8_t *vbase = sm.v() + (tid / CPR - kTile) * L::kRowV + 16 * (tid % CPR);
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
         const int j = tid + S::T * i;
-        if (S::T * (i + 1) <= 2 * S::NK) {   // a whole round of K / V chunks
-            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
+        if (S::T * (i + 1) <= S::NK) {   // a whole round of K chunks
+            *reinterpret_cast<u32x4 *>(kbase + (S::T / CPR) * L::kRow * i) = st.c[i];
+        } else if (S::T * i >= S::NK && S::T * (i + 1) <= 2 * S::NK) {   // of V chunks
+            *reinterpret_cast<u32x4 *>(vbase + (S::T / CPR) * L::kRowV * i) = st.c[i];
+        } else if (j < S::NK) {
+            *reinterpret_cast<u32x4 *>(kbase + (S::T / CPR) * L::kRow * i) = st.c[i];
         } else if (j < 2 * S::NK) {
-            *reinterpret_cast<u32x4 *>(base + (S::T / CPR) * kRow * i) = st.c[i];
+            *reinterpret_cast<u32x4 *>(vbase + (S::T / CPR) * L::kRowV * i) = st.c[i];
         } else if (KV::kScaled && j >= S::KSC && j < S::KSC + 16) {
             *reinterpret_cast<u32x4 *>(sm.ks + 4 * (j - S::KSC)) = st.c[i];
         } else if (KV::kScaled && j >= S::VSC && j < S::VSC + 16) {
@@ -1165,7 +1179,7 @@ template <class KV, int D>
 __device__ __forceinline__ void attend_shared(const DecodeParams &p, const SharedLds<KV, D> &sm,
                                               const typename KV::Q &q, float qs, int nv, int lag,
                                               State<D, 1> &st, const Lane &ln) {
-    constexpr int kRow = SharedLds<KV, D>::kRow;
+    constexpr int kRow = SharedLds<KV, D>::kRow, kRowV = SharedLds<KV, D>::kRowV;
     const bool masked = nv - (p.R - 1) < 2 * 32;   // some row sees < 64 tokens
     const int lim = nv - lag;
 #pragma unroll
@@ -1227,7 +1241,7 @@ __device__ __forceinline__ void attend_shared(const DecodeParams &p, const Share
 #pragma unroll
         for (int blk = 0; blk < D / 16; ++blk)
             st.o[0][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                KV::v_tr(sm.v(), kRow, blk, ln, tok), pb, st.o[0][blk], 0, 0, 0);
+                KV::v_tr(sm.v(), kRowV, blk, ln, tok), pb, st.o[0][blk], 0, 0, 0);
     }
 }
 
