@@ -591,16 +591,22 @@ def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8):
         with torch.cuda.graph(g):
             for r in range(reps):
                 fn((r + 1) % pools)
-        g.replay()
-        torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(3):
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        # untimed replays first, as for the step: at least WARM_GPU_MS of GPU time
+        for _ in range(math.ceil(WARM_GPU_MS / max(a.elapsed_time(b), 1e-3))):
+            g.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(5):
             g.replay()
         b.record(stream)
         b.synchronize()
-        return a.elapsed_time(b) / (3 * reps) * 1e3
+        return a.elapsed_time(b) / (5 * reps) * 1e3
 
     def dyn(pool):
         run.decode(pool)
