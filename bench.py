@@ -277,19 +277,31 @@ def unfused_prologue_us(qkv, pos, slots, w, kp, vp, sc, Hq, Hkv, D, fp8, stream,
     return a.elapsed_time(b) / reps * 1e3
 
 
+def decode_code_sha256() -> str:
+    """sha256 of the decode kernels' source with its // comments and blank
+    lines removed: the code a counter summary measured, which an edit of a
+    comment does not change."""
+    lines = []
+    with open(DECODE_SRC, encoding="utf-8") as f:
+        for line in f:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def traffic_from_profile(workload: str):
     """HBM bytes per decode launch from the committed counter summary of this
-    workload, if there is one and it was taken on the current decode source."""
+    workload, if there is one and it was taken on the current decode code."""
     path = os.path.join(PROFILES, "decode_%s_traffic.md" % workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"decode_source_sha256:\s*([0-9a-f]{64})", text)
+    m = re.search(r"decode_code_sha256:\s*([0-9a-f]{64})", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t:
         return None
-    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    return float(t.group(1)) if sha == m.group(1) else None
+    return float(t.group(1)) if decode_code_sha256() == m.group(1) else None
 
 
 def cpu_baseline(prob, budget_s: float):

@@ -34,8 +34,10 @@
 //     the current one is computed; page ids and descriptors are read through
 //     the scalar memory path (their waits do not count the KV loads), the
 //     next descriptor as soon as the current one is entered;
-//   * each wave keeps its own running max / sum / O; the 4 waves are merged
-//     in LDS at the end of a descriptor.
+//   * each wave keeps its own running max / O and, per lane, the sum of its
+//     own tokens' weights; the column reductions across lanes happen only
+//     when the reference max moves and at the end of a descriptor, where
+//     the 4 waves are merged in LDS.
 // Scores are kept in log2 units (scaled by sm_scale * log2 e) and exp2 is
 // the hardware v_exp_f32; the stored LSE is natural-log.
 #include "common.h"
@@ -1060,12 +1062,15 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
 // The shared-tile path, for 2 .. 4 column blocks (multi-row steps with
 // R G > 16).  Holding every column's O in every wave (the path above) would
 // need NCB x D/4 accumulator registers per lane.  Here a workgroup is NCB
-// waves, wave w owns column block w for all 64 tokens of a tile, and the
-// tile sits in LDS, read by every column block:
-//   * all threads copy the next tile from HBM into registers (16-byte
-//     nontemporal loads) while the waves compute the current one from LDS;
-//   * a barrier, the registers go to LDS (rows padded by 16 bytes, so that
-//     16 lanes reading 16 rows at one column hit distinct banks), a barrier;
+// compute waves, wave w owns column block w for all 64 tokens of a tile, and
+// the tile sits in LDS, read by every column block:
+//   * the next tile is copied from HBM into registers (16-byte nontemporal
+//     loads) while the waves compute the current one from LDS, by all
+//     threads or, for three column blocks at D = 128, by a fourth wave that
+//     only stages (drain_shared_staged);
+//   * a barrier, the registers go to LDS (K rows padded by 16 bytes, so that
+//     16 lanes reading 16 rows at one column hit distinct banks; bf16 V
+//     rows by 32, for the transpose reads), a barrier;
 //   * S^T = K Q^T per 16-token block on v_mfma_f32_16x16x32_{bf16,fp8};
 //     O^T += V^T P^T over 32 tokens per v_mfma_f32_16x16x32_bf16 (the lane's
 //     tokens of two 16-token blocks form its 8 k-slots);
