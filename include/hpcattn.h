@@ -33,8 +33,9 @@
  *
  * Conventions (all entry points):
  *   - Every pointer argument is a DEVICE pointer unless marked "host".
- *   - The caller owns every buffer.  The library allocates, frees and caches
- *     nothing, keeps no global state, never synchronises and never copies
+ *   - The caller owns every buffer.  The library allocates and frees
+ *     nothing, keeps no state between calls (beyond kernel attributes it
+ *     reads once from the runtime), never synchronises and never copies
  *     between host and device.  Work is enqueued on `stream` (a hipStream_t;
  *     NULL is the default stream) and is safe to capture in a HIP graph.
  *   - Return 0 (HPCATTN_OK) or a negative hpcattn_status.  Argument errors
@@ -179,9 +180,11 @@ int hpcattn_plan(const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads,
  * workgroup drains its bin, computing attention over one or more contiguous
  * KV tiles per descriptor and writing a partial output with its log-sum-exp).
  *
- * Launches map->num_bins workgroups (256 threads, or 64 per 16 query rows
- * of a KV head when q_rows * G > 16); bin i is drained by workgroup i.
- * Writes part_o / part_lse rows 0 .. num_desc - 1 and nothing else.  dims->batch and dims->num_kv_heads must equal the map's.
+ * Launches map->num_bins workgroups, bin i drained by workgroup i: 256
+ * threads, or when q_rows * G > 16 64 per 16 query rows of a KV head (plus
+ * a 64-thread staging wave for 33 .. 48 rows at head_dim 128).  Writes
+ * part_o / part_lse rows 0 .. num_desc - 1 and nothing else.  dims->batch
+ * and dims->num_kv_heads must equal the map's.
  * q_scale, k_scale, v_scale: NULL for bf16, required for fp8.
  * part_o / part_lse: at least hpcattn_max_partials(B, H_kv, P) rows;
  * part_o_rows gives the caller's row capacity.
