@@ -256,8 +256,8 @@ int hpcattn_decode_combine(const hpcattn_dims *dims, const void *q, const float 
  *   the grid reserves ceil(max_seq_len / C) chunks per (request, KV head)
  *   and chunk k owns tokens [k C, (k + 1) C) clipped to the length.
  * max_seq_len (host) bounds every seq_lens[b] and sizes the policy-1 grid.
- * One workgroup of 256 threads per (request, KV head, split); empty splits
- * write lse = -inf.  Then the combine runs over the fixed splits and writes
+ * One workgroup per (request, KV head, split), of the same size as the
+ * dynamic decode's; empty splits write lse = -inf.  Then the combine runs over the fixed splits and writes
  * out / out_lse like hpcattn_combine.  part_o / part_lse need
  * hpcattn_static_max_partials() rows (given in part_o_rows).
  */
