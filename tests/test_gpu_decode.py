@@ -188,3 +188,26 @@ def test_full_size_configs_sampled(R, name, npairs):
         compare(run.out, run.out_lse, ref_o, ref_l, rows_of(pairs, prob.workload.group),
                 prob.workload.kv_dtype == "fp8", "%s layer %d" % (name, layer))
         del h, ref_o, ref_l
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_maximum_batch(R, kv):
+    """The largest batch the library takes (8192 requests), ragged lengths
+    from 0 to 300 tokens, through plan -> decode -> combine and through the
+    fused call, against the oracle on every request."""
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 301, size=8192).astype(np.int32)
+    lens[::97] = 0                      # empty requests among them
+    w = custom_workload(1, 4, 64, kv, P=1024, m=1)
+    prob = wl.make_problem("tiny", seed=3, device="cuda", lens=lens, poison=True, workload=w)
+    assert len(prob.seq_lens) == 8192
+    _, run = run_and_compare(R, prob, "max batch %s, two launches" % kv, P=1024, m=1)
+    out2, lse2 = run.out.clone(), run.out_lse.clone()
+    run.decode_combine(0)
+    sync()
+    # the fused call agrees with decode + combine (up to the merge order)
+    assert torch.allclose(run.out.float(), out2.float(), atol=2e-2, rtol=0)
+    fin = torch.isfinite(lse2)
+    assert torch.equal(torch.isfinite(run.out_lse), fin)
+    assert torch.allclose(run.out_lse[fin], lse2[fin], atol=1e-4, rtol=0)
+    assert int(run.tickets.abs().sum()) == 0
