@@ -21,8 +21,12 @@ def R():
 
 
 @pytest.mark.parametrize("name,lens", [("tiny", None), ("mixed", [300, 4096, 17, 20000, 65]),
-                                       ("fp8", [1000, 70, 5000])])
+                                       ("fp8", [1000, 70, 5000]),
+                                       ("mtp", [300, 4096, 17, 2000, 65]),
+                                       ("mtp_fp8", [1000, 70, 5000])])
 def test_graph_replay_matches_eager(R, name, lens):
+    # mtp / mtp_fp8: 6 query rows of 8 heads, the shared-tile kernel with its
+    # staging wave
     prob = wl.make_problem(name, seed=11, device="cuda", layers=2,
                            lens=None if lens is None else np.array(lens, np.int32))
     run = R.DecodeRunner(prob)
