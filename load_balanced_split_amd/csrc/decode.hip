@@ -1573,21 +1573,31 @@ constexpr int staging_wave(int ncb) {
 // 1.5 times as long.  k = (4 occ - 3) / 3 workgroups leave room for any
 // placement of one more workgroup's waves: three at three waves per SIMD,
 // four at four.  Computed once per instance from its register count.
+//
+// The bf16 staging-wave workgroup is held to two per CU, below the three
+// its registers admit: with 6 rows of 8 heads, decode + combine ran 1-2%
+// faster at two (one process, the same buffers: 311.1 vs 318.4 us and
+// 308.0 vs 312.4 us on two boxes), with fewer partials to combine.
 constexpr int kLdsPerCu = 160 * 1024;
 
 template <class KV, int D, int NCB, int SW>
 unsigned shared_lds_pad() {
-    if constexpr (NCB + SW != 3) {
+    constexpr bool staged_bf16 = SW != 0 && !KV::kScaled;
+    if constexpr (NCB + SW != 3 && !staged_bf16) {
         return 0u;
     } else {
         static const unsigned pad = [] {
-            hipFuncAttributes a{};
-            if (hipFuncGetAttributes(&a, (const void *)decode_shared_kernel<KV, D, NCB, SW>) !=
-                hipSuccess)
-                return 0u;
-            const int regs = (max(a.numRegs, 1) + 7) / 8 * 8;   // allocation granule
-            const int occ = min(8, 512 / regs);                  // waves per SIMD
-            const int k = max(1, (4 * occ - 3) / 3);
+            int k = 2;
+            if constexpr (!staged_bf16) {
+                hipFuncAttributes a{};
+                if (hipFuncGetAttributes(&a,
+                                         (const void *)decode_shared_kernel<KV, D, NCB, SW>) !=
+                    hipSuccess)
+                    return 0u;
+                const int regs = (max(a.numRegs, 1) + 7) / 8 * 8;   // allocation granule
+                const int occ = min(8, 512 / regs);                  // waves per SIMD
+                k = max(1, (4 * occ - 3) / 3);
+            }
             const int want = kLdsPerCu / k - (int)sizeof(SharedLds<KV, D>);
             return want > 0 ? (unsigned)want & ~1023u : 0u;
         }();
