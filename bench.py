@@ -77,6 +77,10 @@ def parse_args():
     ap.add_argument("--ablation", action="store_true",
                     help="also sweep the static split-KV baseline on the same inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-ms", type=float, default=FIRST_WARM_GPU_MS,
+                    help="least GPU time (ms) of untimed step replays before the first timed "
+                         "region; later regions get min(this, %g) (0 under rocprofv3 --pmc, "
+                         "which serialises every dispatch)" % WARM_GPU_MS)
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying the step "
                          "from a HIP graph")
@@ -440,7 +444,8 @@ def main():
     # started right after another, 8380 us after 2 s).
     # Events between replays give the spread of the per-step time.
     per_graph = 1 if layers >= pools else pools // layers
-    warm_ms = [FIRST_WARM_GPU_MS]   # the first timed region of the process, then WARM_GPU_MS
+    warm_later = min(WARM_GPU_MS, args.warm_ms)
+    warm_ms = [args.warm_ms]   # the first timed region of the process, then warm_later
 
     def timed(one_step):
         """(ms for all K steps, per-step ms of each replay, host seconds)."""
@@ -465,7 +470,7 @@ def main():
             for _ in range(max(-(-args.warmup // per_graph),
                                math.ceil(warm_ms[0] / per_replay_ms))):
                 g.replay()
-            warm_ms[0] = WARM_GPU_MS
+            warm_ms[0] = warm_later
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(chunks) + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -549,7 +554,8 @@ def main():
     }
 
     if args.ablation:
-        out["ablation"] = static_sweep(run, prob, layers, pools, stream, dec_avg)
+        out["ablation"] = static_sweep(run, prob, layers, pools, stream, dec_avg,
+                                       warm_ms=min(WARM_GPU_MS, args.warm_ms))
     if w.q_rows > 1:
         out["multi_row"] = rows_as_requests(prob, layers, pools, t_step, dec_avg, capture,
                                             graph_avg_ms, args)
@@ -597,7 +603,8 @@ def rows_as_requests(prob, layers, pools, step_ms, dec_ms, capture, graph_avg_ms
             "decode_speedup_vs_rows_as_requests": round(dec / dec_ms, 3)}
 
 
-def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8):
+def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8,
+                 warm_ms=WARM_GPU_MS):
     """Time the static split-KV baseline (decode + combine) at every sweep
     point against dynamic decode + combine on the same pools, each as a HIP
     graph of `reps` back-to-back calls rotating over the pools."""
@@ -617,7 +624,7 @@ def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8):
         b.record(stream)
         b.synchronize()
         # untimed replays first, as for the step: at least WARM_GPU_MS of GPU time
-        for _ in range(math.ceil(WARM_GPU_MS / max(a.elapsed_time(b), 1e-3))):
+        for _ in range(math.ceil(warm_ms / max(a.elapsed_time(b), 1e-3))):
             g.replay()
         torch.cuda.synchronize()
         a.record(stream)
