@@ -410,13 +410,23 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def graph_avg_ms(fn, count, reps=5):
+    def graph_avg_ms(fn, count, reps=5, warm=0.0):
         """Average GPU time of one of the `count` launches fn() enqueues, from
-        HIP events around replays of a graph holding them back to back."""
+        HIP events around replays of a graph holding them back to back,
+        after untimed replays for at least `warm` ms of GPU time.  The decode
+        graphs are warmed (the capture leaves the GPU idle, as for the step
+        below); the short combine and plan launches are not: 100 ms of them
+        alone measured the combine at twice its time inside the step, so
+        they are timed right after the warm decode graph instead."""
         g = capture(fn)
-        g.replay()
-        torch.cuda.synchronize()
         a, b = events()
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        for _ in range(math.ceil(warm / max(a.elapsed_time(b), 1e-3))):
+            g.replay()
+        torch.cuda.synchronize()
         a.record(stream)
         for _ in range(reps):
             g.replay()
@@ -498,9 +508,11 @@ def main():
 
     # Per-kernel GPU time, each kernel back to back in its own graph.
     n_dec = max(layers, pools) if multi_layer else pools
-    dec_avg = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec)
+    fused_avg = graph_avg_ms(lambda: [run.decode_combine(i % pools) for i in range(n_dec)], n_dec,
+                             warm=warm_later)
+    dec_avg = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec,
+                           warm=warm_later)
     combine_ms = graph_avg_ms(lambda: [run.combine() for _ in range(16)], 16)
-    fused_avg = graph_avg_ms(lambda: [run.decode_combine(i % pools) for i in range(n_dec)], n_dec)
     plan_ms = graph_avg_ms(lambda: [run.plan() for _ in range(16)], 16)
     torch.cuda.synchronize()
 
@@ -593,9 +605,10 @@ def rows_as_requests(prob, layers, pools, step_ms, dec_ms, capture, graph_avg_ms
             run.combine()
 
     step()
-    per = graph_avg_ms(step, 1, reps=max(2, min(10, args.steps)))
+    warm = min(WARM_GPU_MS, args.warm_ms)   # warmed like the step and decode it is set against
+    per = graph_avg_ms(step, 1, reps=max(2, min(10, args.steps)), warm=warm)
     n_dec = max(layers, pools)
-    dec = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec)
+    dec = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec, warm=warm)
     return {"rows": R,
             "rows_as_requests_us_per_step": round(per * 1e3, 1),
             "rows_as_requests_decode_avg_us": round(dec * 1e3, 2),
