@@ -211,3 +211,19 @@ def test_maximum_batch(R, kv):
     assert torch.equal(torch.isfinite(run.out_lse), fin)
     assert torch.allclose(run.out_lse[fin], lse2[fin], atol=1e-4, rtol=0)
     assert int(run.tickets.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("kv,rows,per_cu", [("bf16", 8, 2), ("fp8", 8, 3),
+                                            ("bf16", 48, 2), ("fp8", 48, 4)])
+def test_suggested_bins_are_the_measured_residency(kv, rows, per_cu):
+    """The default bin count is CUs x the workgroups each CU holds: two for
+    the one-row bf16 kernel (LDS padding holds it there; its registers would
+    admit three), three for one-row fp8, and for 6 rows of 8 heads (the
+    shared-tile kernel with its staging wave) two for bf16 and four for fp8.
+    A change to a kernel's registers or LDS that moves these fails here."""
+    from load_balanced_split_amd import hpcattn as H
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    code = H.KV_BF16 if kv == "bf16" else H.KV_FP8_E4M3
+    n = H.hpcattn_suggest_num_bins(128, code, rows)
+    say("suggested bins", kv, "rows", rows, "->", n, "on", cus, "CUs")
+    assert n == cus * per_cu
