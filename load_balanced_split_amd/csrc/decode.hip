@@ -1499,9 +1499,17 @@ static_decode_kernel(DecodeParams p) {
 }
 
 // Shared-tile kernels (2 .. 4 column blocks): NCB compute waves per
-// workgroup, plus a staging wave when SW, sized for three waves per SIMD.
+// workgroup, plus a staging wave when SW, sized for three waves per SIMD;
+// the bf16 instance with two column blocks and no staging wave needs 176
+// registers and runs at two.
 template <class KV, int D, int NCB, int SW>
-__global__ void __launch_bounds__(64 * (NCB + SW)) __attribute__((amdgpu_waves_per_eu(3)))
+constexpr int shared_waves_per_eu() {
+    return (!KV::kScaled && D == 128 && NCB == 2 && SW == 0) ? 2 : 3;
+}
+
+template <class KV, int D, int NCB, int SW>
+__global__ void __launch_bounds__(64 * (NCB + SW))
+__attribute__((amdgpu_waves_per_eu(shared_waves_per_eu<KV, D, NCB, SW>())))
 decode_shared_kernel(DecodeParams p) {
     __shared__ SharedLds<KV, D> sm;
     const MapLayout lay(p.B, p.Hkv, p.P);
