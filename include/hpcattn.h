@@ -271,7 +271,8 @@ int hpcattn_static_decode(const hpcattn_dims *dims, int32_t policy, int32_t para
                           void *stream);
 
 /* Partial rows hpcattn_static_decode needs: B * H_kv * splits, where splits
- * is S (policy 0) or ceil(max_seq_len / C) (policy 1); 0 on bad input. */
+ * is S (policy 0) or ceil(max_seq_len / C) (policy 1); 0 on bad input or
+ * when that exceeds INT32_MAX rows (hpcattn_static_decode rejects it). */
 int64_t hpcattn_static_max_partials(int32_t batch, int32_t num_kv_heads, int32_t policy,
                                     int32_t param, int32_t max_seq_len);
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "hpcattn.h"
+#include "layout.h"
 
 namespace hpcattn {
 
@@ -12,19 +13,6 @@ constexpr int kTile = HPCATTN_PAGE_SIZE;  // tokens per tile and per page
 constexpr int kWaves = 4;                 // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kWaves;
 constexpr int kPlanThreads = 1024;
-
-// Word offsets inside a task map (layout documented in hpcattn.h).
-struct MapLayout {
-    int64_t lens, bin_off, seg_off, desc, words;
-    __host__ __device__ MapLayout(int32_t B, int32_t Hkv, int32_t P) {
-        const int64_t S = (int64_t)B * Hkv;
-        lens = 8;
-        bin_off = lens + B;
-        seg_off = bin_off + (int64_t)P + 1;
-        desc = seg_off + S + 1;
-        words = desc + 4 * (S + P - 1);
-    }
-};
 
 // Arguments of the decode kernels (dynamic and static), passed by value.
 struct DecodeParams {

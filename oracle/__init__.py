@@ -72,8 +72,10 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_LIB_PATH)
+            # ORACLE_LIB names another build of oracle.c (the sanitizer run of
+            # the test suite builds one with -fsanitize=address,undefined).
+            path = os.environ.get("ORACLE_LIB") or build()
+            lib = ctypes.CDLL(path)
             P = ctypes.c_void_p
             i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
             dp = ctypes.POINTER(_Dims)

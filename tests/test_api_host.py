@@ -111,6 +111,9 @@ def test_decode_rejects_bad_arguments(H):
     assert _decode(H, _dims(H, q_rows=0), m) == H.ERR_SHAPE       # at least one row
     assert _decode(H, _dims(H, q_rows=17), m) == H.ERR_SHAPE      # R G = 68 > 64 rows
     assert _decode(H, _dims(H, num_q_heads=16, q_rows=5), m) == H.ERR_SHAPE   # 80 rows
+    # q_rows * G taken in int32 would wrap to 16 rows and pass: rejected, no launch
+    assert _decode(H, _dims(H, num_q_heads=16, q_rows=2 ** 28 + 1), m) == H.ERR_SHAPE
+    assert _decode(H, _dims(H, num_q_heads=16, q_rows=2 ** 31 - 1), m) == H.ERR_SHAPE
     assert _decode(H, _dims(H), m, rows=4 * 1 + 8 - 2) == H.ERR_WORKSPACE
     small = _map(H, nbytes=16)
     assert _decode(H, _dims(H), small) == H.ERR_WORKSPACE
@@ -193,6 +196,10 @@ def test_prologue_rejects_bad_arguments(H):
     assert pro(nulls=("pos",)) == H.ERR_NULL             # RoPE needs positions
     assert pro(fp8=True, scales=False) == H.ERR_DTYPE     # fp8 needs scales
     assert pro(fp8=False, scales=True) == H.ERR_DTYPE     # bf16 takes none
+    # H_q + 2 H_kv taken in int32 would wrap negative and pass the row bound
+    big = H.hpcattn_prologue_dims(4, 2 ** 31 - 1, 2 ** 30, 128, 4, H.KV_BF16, 1, 1e-6, 1e4)
+    assert lib.hpcattn_prologue(ctypes.byref(big), FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                FAKE, FAKE, None, None, None) == H.ERR_SHAPE
 
 
 def test_strerror_covers_every_status(H):
