@@ -5,9 +5,11 @@ once, then hpcattn_decode + hpcattn_combine for every layer, each layer with
 its own KV pool (so the 256 MB Infinity Cache cannot serve repeats).  Inputs
 are resident in HBM before the timed region starts.
 
-    python bench.py [--steps K] [--warmup W]
-                    [--workload mixed|single_long|heavy_tail|fp8|mtp|mtp_fp8|prologue]
-                    [--num-bins P] [--min-tiles m] [--ablation] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--num-bins P]
+                    [--min-tiles m] [--ablation] [--no-cpu-baseline] [--no-extras]
+
+NAME: mixed (default), single_long, heavy_tail, heavy_tail_long_first,
+heavy_tail_long_last, fp8, mtp, mtp_fp8, mixed_shard, or prologue.
 
 Prints one JSON line.  `value` is the step's KV-read throughput (live KV
 bytes of all layers / step time), the step replayed from a HIP graph as a
@@ -15,7 +17,10 @@ serving loop would (--eager launches each kernel from the host instead);
 `roofline` is for the decode kernel, its average launch time taken with HIP
 events around a graph of back-to-back decode launches on the stream they run
 on; `cpu_baseline` is the fp64 oracle on the host cores over a bounded sample
-of the same workload.
+of the same workload.  The default (mixed) run then adds `heavy_tail`: the
+heavy-tail batch in its three orders, dynamic decode + combine (two launches
+and fused) against every point of the static split-KV sweep; and
+`mixed_shard`: the step at one GPU's head shard of the mixed batch.
 """
 from __future__ import annotations
 
@@ -47,6 +52,15 @@ DESCRIPTIONS = {
                    "bf16, page 64, shuffled pages, 4 rotating KV pools",
     "heavy_tail": "heavy-tail: 120 requests of 1024+-10% and 8 of 65536 tokens, 8 KV / 64 Q "
                   "heads, head_dim 128, bf16, page 64, 4 rotating KV pools",
+    "heavy_tail_long_first": "heavy-tail, long requests first: the heavy-tail lengths with "
+                             "the 8 requests of 65536 tokens at batch positions 0-7, 8 KV / "
+                             "64 Q heads, head_dim 128, bf16, page 64, 4 rotating KV pools",
+    "heavy_tail_long_last": "heavy-tail, long requests last: the heavy-tail lengths with the 8 "
+                            "requests of 65536 tokens at batch positions 120-127, 8 KV / 64 Q "
+                            "heads, head_dim 128, bf16, page 64, 4 rotating KV pools",
+    "mixed_shard": "mixed-length head shard (one GPU of 8-way head parallelism): 64 requests, "
+                   "KV lens log-uniform in [256, 32768] (seed 0), 1 KV / 8 Q heads, head_dim "
+                   "128, bf16, page 64, 32 layers with distinct KV pools, one task map per step",
     "fp8": "fp8 KV: 32 requests, KV lens log-uniform in [1024, 131072], 8 KV / 64 Q heads, "
            "head_dim 128, e4m3 Q/K/V with per-token per-head fp32 scales, page 64, "
            "4 rotating KV pools",
@@ -59,6 +73,11 @@ DESCRIPTIONS = {
                "heads, head_dim 128, e4m3 Q/K/V with per-token per-head fp32 scales, page 64, "
                "4 rotating KV pools",
 }
+
+
+def note(*a):
+    """A progress line on stderr (the JSON result alone goes to stdout)."""
+    print("#", *a, file=sys.stderr, flush=True)
 
 
 def parse_args():
@@ -77,6 +96,9 @@ def parse_args():
     ap.add_argument("--ablation", action="store_true",
                     help="also sweep the static split-KV baseline on the same inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="with the mixed workload: skip the heavy-tail order sweep and the "
+                         "head-shard step that follow the headline")
     ap.add_argument("--warm-ms", type=float, default=FIRST_WARM_GPU_MS,
                     help="least GPU time (ms) of untimed step replays before the first timed "
                          "region; later regions get min(this, %g) (0 under rocprofv3 --pmc, "
@@ -361,34 +383,124 @@ def cpu_baseline(prob, budget_s: float):
                                         % (n1, tok1, spent1)}}
 
 
-def main():
-    args = parse_args()
-    if args.calibrate:
-        calibrate()
-        return
-    if args.workload == "prologue":
-        prologue_bench()
-        return
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only: the library has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+class Clock:
+    """HIP-event timing on one stream: graph capture, warm averages of
+    back-to-back launches, and the timed region of K steps.
 
-    import numpy as np
+    Warm-up: a GPU left idle by a capture needs some milliseconds to return
+    to its running speed (about 25 ms of work on the draft-verify fp8
+    workload, whose first 20 steps ran 15% slower than the next ones), and a
+    process's first second or so of GPU work can run slower still (the mixed
+    step measured 8730 us after 100 ms of warm-up in a process started right
+    after another, 8380 us after 2 s).  So the first timed region of the
+    process follows untimed replays of at least `first_warm_ms` of GPU time,
+    later ones at least min(WARM_GPU_MS, first_warm_ms)."""
+
+    def __init__(self, stream, first_warm_ms, eager=False):
+        self.stream = stream
+        self.warm_later = min(WARM_GPU_MS, first_warm_ms)
+        self.next_warm = first_warm_ms
+        self.eager = eager
+
+    def events(self):
+        import torch
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def capture(self, fn):
+        """Capture fn's launches into a HIP graph on torch's capture stream."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def graph_avg_ms(self, fn, count, reps=5, warm=0.0):
+        """Average GPU time of one of the `count` launches fn() enqueues, from
+        HIP events around replays of a graph holding them back to back,
+        after untimed replays for at least `warm` ms of GPU time.  The decode
+        graphs are warmed (the capture leaves the GPU idle, as for the step);
+        the short combine and plan launches are not: 100 ms of them alone
+        measured the combine at twice its time inside the step, so they are
+        timed right after a warm decode graph instead."""
+        import torch
+        g = self.capture(fn)
+        a, b = self.events()
+        a.record(self.stream)
+        g.replay()
+        b.record(self.stream)
+        b.synchronize()
+        for _ in range(math.ceil(warm / max(a.elapsed_time(b), 1e-3))):
+            g.replay()
+        torch.cuda.synchronize()
+        a.record(self.stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(self.stream)
+        b.synchronize()
+        return a.elapsed_time(b) / (reps * count)
+
+    def timed(self, one_step, steps, warmup, per_graph):
+        """Exactly `steps` steps enqueued back to back with no host
+        synchronisation between them (as a serving loop enqueues its steps),
+        bracketed by a synchronize on each side.  Graph mode replays a graph
+        of `per_graph` consecutive steps (so that one-layer workloads still
+        rotate over their KV pools) and a one-step graph for any remainder;
+        the captured graph first runs untimed for `warmup` steps and the warm
+        time.  Events between replays give the spread of the step time.
+        Returns (ms for all steps, per-step ms of each replay, host s)."""
+        import torch
+        if self.eager:
+            chunks = [(lambda k=k: one_step(warmup + k), 1) for k in range(steps)]
+        else:
+            full, rem = divmod(steps, per_graph)
+            chunks = []
+            g = self.capture(lambda: [one_step(k) for k in range(per_graph)])
+            if full:
+                chunks += [(g.replay, per_graph)] * full
+            if rem:
+                g1 = self.capture(lambda: one_step(0))
+                g1.replay()
+                chunks += [(g1.replay, 1)] * rem
+            a, b = self.events()
+            a.record(self.stream)
+            g.replay()
+            b.record(self.stream)
+            b.synchronize()
+            per_replay_ms = max(a.elapsed_time(b), 1e-3)
+            for _ in range(max(-(-warmup // per_graph),
+                               math.ceil(self.next_warm / per_replay_ms))):
+                g.replay()
+            self.next_warm = self.warm_later
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(chunks) + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record(self.stream)
+        for i, (run_chunk, _) in enumerate(chunks):
+            run_chunk()
+            evs[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        host_s = time.perf_counter() - t0
+        per = [evs[i].elapsed_time(evs[i + 1]) / n for i, (_, n) in enumerate(chunks)]
+        return evs[0].elapsed_time(evs[-1]), per, host_s
+
+
+def measure(name, args, clock, steps, warmup, layers=None):
+    """Time one workload's step (plan once, then decode + combine per layer)
+    as two launches per layer and fused, and its kernels on their own.
+    Returns (result dict, runner, problem)."""
     import torch
 
-    from load_balanced_split_amd import hpcattn as H
     from load_balanced_split_amd import runner, workloads as wl
 
-    torch.cuda.set_device(0)
-    name = args.workload
+    note("measuring", name)
     w = wl.WORKLOADS[name]
     multi_layer = w.layers > 1
-    layers = args.layers if args.layers is not None else (w.layers if multi_layer else 1)
+    if layers is None:
+        layers = args.layers if args.layers is not None else (w.layers if multi_layer else 1)
     pools = layers if multi_layer else max(1, args.pools)
     prob = wl.make_problem(name, seed=args.seed, device="cuda", layers=pools)
     run = runner.DecodeRunner(prob, num_bins=args.num_bins, min_tiles=args.min_tiles)
-    stream = torch.cuda.current_stream()
     live_tokens = int(prob.seq_lens.sum())
     kv_bytes_layer = live_tokens * wl.kv_bytes_per_token(w)
 
@@ -399,132 +511,40 @@ def main():
             run.decode((k * layers + layer) % pools)
             run.combine()
 
-    def events():
-        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def capture(fn):
-        """Capture fn's launches into a HIP graph on torch's capture stream."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        torch.cuda.synchronize()
-        return g
-
-    def graph_avg_ms(fn, count, reps=5, warm=0.0):
-        """Average GPU time of one of the `count` launches fn() enqueues, from
-        HIP events around replays of a graph holding them back to back,
-        after untimed replays for at least `warm` ms of GPU time.  The decode
-        graphs are warmed (the capture leaves the GPU idle, as for the step
-        below); the short combine and plan launches are not: 100 ms of them
-        alone measured the combine at twice its time inside the step, so
-        they are timed right after the warm decode graph instead."""
-        g = capture(fn)
-        a, b = events()
-        a.record(stream)
-        g.replay()
-        b.record(stream)
-        b.synchronize()
-        for _ in range(math.ceil(warm / max(a.elapsed_time(b), 1e-3))):
-            g.replay()
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
-            g.replay()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / (reps * count)
-
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-
-    # The timed region: exactly K steps, enqueued back to back with no host
-    # synchronisation between them (as a serving loop enqueues its steps),
-    # bracketed by a synchronize on each side.  Graph mode replays a graph of
-    # `per_graph` consecutive steps, so that the one-layer workloads still
-    # rotate over their pools, and a one-step graph for any remainder.  The
-    # captured graph first runs W untimed steps of its own, right before the
-    # timed region, for W steps and at least WARM_GPU_MS of GPU time: a GPU
-    # left idle by the capture needs some milliseconds to return to its
-    # running speed (about 25 ms of work on the draft-verify fp8 workload,
-    # whose first 20 steps ran 15% slower than the next ones).  Before the
-    # first timed region of the process the replays last FIRST_WARM_GPU_MS:
-    # a process's first second or so of GPU work can run slower still (the
-    # mixed step measured 8730 us after 100 ms of warm-up in a process
-    # started right after another, 8380 us after 2 s).
-    # Events between replays give the spread of the per-step time.
-    per_graph = 1 if layers >= pools else pools // layers
-    warm_later = min(WARM_GPU_MS, args.warm_ms)
-    warm_ms = [args.warm_ms]   # the first timed region of the process, then warm_later
-
-    def timed(one_step):
-        """(ms for all K steps, per-step ms of each replay, host seconds)."""
-        if args.eager:
-            chunks = [(lambda k=k: one_step(args.warmup + k), 1) for k in range(args.steps)]
-        else:
-            full, rem = divmod(args.steps, per_graph)
-            chunks = []
-            g = capture(lambda: [one_step(k) for k in range(per_graph)])
-            if full:
-                chunks += [(g.replay, per_graph)] * full
-            if rem:
-                g1 = capture(lambda: one_step(0))
-                g1.replay()
-                chunks += [(g1.replay, 1)] * rem
-            a, b = events()
-            a.record(stream)
-            g.replay()
-            b.record(stream)
-            b.synchronize()
-            per_replay_ms = max(a.elapsed_time(b), 1e-3)
-            for _ in range(max(-(-args.warmup // per_graph),
-                               math.ceil(warm_ms[0] / per_replay_ms))):
-                g.replay()
-            warm_ms[0] = warm_later
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(chunks) + 1)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        evs[0].record(stream)
-        for i, (run_chunk, _) in enumerate(chunks):
-            run_chunk()
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        host_s = time.perf_counter() - t0
-        per = [evs[i].elapsed_time(evs[i + 1]) / n for i, (_, n) in enumerate(chunks)]
-        return evs[0].elapsed_time(evs[-1]), per, host_s
-
-    total_ms, step_ms, wall = timed(step)
-    t_step = total_ms / args.steps
-
-    # The same step with decode and combine fused into one launch per layer
-    # (hpcattn_decode_combine), timed the same way.
     def fused_step(k):
+        """The same step with decode and combine in one launch per layer."""
         run.plan()
         for layer in range(layers):
             run.decode_combine((k * layers + layer) % pools)
 
-    total_fused_ms, _, _ = timed(fused_step)
-    t_fused = total_fused_ms / args.steps
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    per_graph = 1 if layers >= pools else pools // layers
+    total_ms, step_ms, wall = clock.timed(step, steps, warmup, per_graph)
+    t_step = total_ms / steps
+    total_fused_ms, _, _ = clock.timed(fused_step, steps, warmup, per_graph)
+    t_fused = total_fused_ms / steps
 
     # Per-kernel GPU time, each kernel back to back in its own graph.
     n_dec = max(layers, pools) if multi_layer else pools
-    fused_avg = graph_avg_ms(lambda: [run.decode_combine(i % pools) for i in range(n_dec)], n_dec,
-                             warm=warm_later)
-    dec_avg = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec,
-                           warm=warm_later)
-    combine_ms = graph_avg_ms(lambda: [run.combine() for _ in range(16)], 16)
-    plan_ms = graph_avg_ms(lambda: [run.plan() for _ in range(16)], 16)
+    fused_avg = clock.graph_avg_ms(lambda: [run.decode_combine(i % pools) for i in range(n_dec)],
+                                   n_dec, warm=clock.warm_later)
+    dec_avg = clock.graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec,
+                                 warm=clock.warm_later)
+    combine_ms = clock.graph_avg_ms(lambda: [run.combine() for _ in range(16)], 16)
+    plan_ms = clock.graph_avg_ms(lambda: [run.plan() for _ in range(16)], 16)
     torch.cuda.synchronize()
 
     value = kv_bytes_layer * layers / (t_step * 1e-3) / 1e9
     achieved = kv_bytes_layer / (dec_avg * 1e-3) / 1e9
-    out = {
+    res = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(t_step, 4),
         "us_per_step": round(t_step * 1e3, 1),
         "higher_is_better": True,
@@ -545,13 +565,18 @@ def main():
             "q_rows": w.q_rows,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        # Each kernel's average comes from its own graph of back-to-back
+        # launches, so the residual (step - plan - layers x (decode +
+        # combine)) is the launch overhead inside the step minus what the
+        # isolated averages over-count; it can come out negative.
         "breakdown_us": {"plan": round(plan_ms * 1e3, 2),
                          "decode_avg": round(dec_avg * 1e3, 2),
                          "combine": round(combine_ms * 1e3, 2),
-                         "launch_gaps": round((t_step - plan_ms - layers * (dec_avg + combine_ms))
-                                              * 1e3, 1),
+                         "residual": round((t_step - plan_ms - layers * (dec_avg + combine_ms))
+                                           * 1e3, 1),
                          "step_min": round(min(step_ms) * 1e3, 1),
-                         "step_p90": round(sorted(step_ms)[int(0.9 * (len(step_ms) - 1))] * 1e3, 1)},
+                         "step_p90": round(sorted(step_ms)[int(0.9 * (len(step_ms) - 1))] * 1e3,
+                                           1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(name),
@@ -564,20 +589,92 @@ def main():
         "wall_s_timed": round(wall, 3),
         "launch": "eager" if args.eager else "hip_graph (%d step(s) per replay)" % per_graph,
     }
+    res["_layers"], res["_pools"], res["_dec_avg"] = layers, pools, dec_avg
+    return res, run, prob
+
+
+def heavy_tail_orders(args, clock):
+    """The heavy-tail batch in its three orders (the 8 long requests at seeded
+    random positions, first, last): dynamic decode + combine as two launches
+    and fused, against every point of the static split-KV sweep, each as a
+    graph of back-to-back calls rotating over the KV pools."""
+    import torch
+
+    from load_balanced_split_amd import runner, workloads as wl
+
+    res = {"workload": DESCRIPTIONS["heavy_tail"], "target_speedup_vs_best_static": 1.5}
+    for order, name in (("random", "heavy_tail"), ("long_first", "heavy_tail_long_first"),
+                        ("long_last", "heavy_tail_long_last")):
+        note("heavy-tail order", order, "with the static sweep")
+        prob = wl.make_problem(name, seed=args.seed, device="cuda", layers=max(1, args.pools))
+        run = runner.DecodeRunner(prob, num_bins=args.num_bins, min_tiles=args.min_tiles)
+        sw = static_sweep(run, prob, 1, max(1, args.pools), clock)
+        kv = int(prob.seq_lens.sum()) * wl.kv_bytes_per_token(prob.workload)
+        sw["kv_gbs_two_launches"] = round(kv / (sw["dynamic_us"] * 1e-6) / 1e9, 1)
+        sw["kv_gbs_fused"] = round(kv / (sw["dynamic_fused_us"] * 1e-6) / 1e9, 1)
+        res[order] = sw
+        del run, prob
+        torch.cuda.empty_cache()
+    best = max(res["random"]["speedup_vs_best_static"],
+               res["random"]["fused_speedup_vs_best_static"])
+    res["random_best_speedup"] = best
+    res["target_met"] = best >= 1.5
+    return res
+
+
+def shard_step(args, clock):
+    """One GPU's head shard of the mixed batch (1 KV head, 8 query heads,
+    32 layers): the step timed like the headline's, in a compact record."""
+    import torch
+    steps = max(5, min(args.steps, 20))
+    r, run, prob = measure("mixed_shard", args, clock, steps, min(args.warmup, 5))
+    del run, prob
+    torch.cuda.empty_cache()
+    return {"workload": DESCRIPTIONS["mixed_shard"], "steps": steps,
+            "us_per_step": r["us_per_step"], "kv_gbs": r["value"],
+            "pct_hbm_peak": r["pct_hbm_peak"], "breakdown_us": r["breakdown_us"],
+            "decode_roofline_frac": r["roofline"]["frac"], "fused": r["fused"],
+            "num_bins": r["config"]["num_bins"], "num_desc": r["config"]["num_desc"],
+            "kv_bytes_per_layer": r["config"]["kv_bytes_per_layer"]}
+
+
+def main():
+    args = parse_args()
+    if args.calibrate:
+        calibrate()
+        return
+    if args.workload == "prologue":
+        prologue_bench()
+        return
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    torch.cuda.set_device(0)
+    clock = Clock(torch.cuda.current_stream(), args.warm_ms, args.eager)
+    out, run, prob = measure(args.workload, args, clock, args.steps, args.warmup)
+    layers, pools, dec_avg = out.pop("_layers"), out.pop("_pools"), out.pop("_dec_avg")
 
     if args.ablation:
-        out["ablation"] = static_sweep(run, prob, layers, pools, stream, dec_avg,
-                                       warm_ms=min(WARM_GPU_MS, args.warm_ms))
-    if w.q_rows > 1:
-        out["multi_row"] = rows_as_requests(prob, layers, pools, t_step, dec_avg, capture,
-                                            graph_avg_ms, args)
-
+        out["ablation"] = static_sweep(run, prob, layers, pools, clock)
+    if prob.workload.q_rows > 1:
+        out["multi_row"] = rows_as_requests(prob, layers, pools, out["ms_per_step"], dec_avg,
+                                            clock, args)
     if not args.no_cpu_baseline:
+        note("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+    if args.workload == "mixed" and not args.no_extras:
+        del run, prob
+        torch.cuda.empty_cache()
+        out["heavy_tail"] = heavy_tail_orders(args, clock)
+        out["mixed_shard"] = shard_step(args, clock)
     print(json.dumps(out), flush=True)
 
 
-def rows_as_requests(prob, layers, pools, step_ms, dec_ms, capture, graph_avg_ms, args):
+def rows_as_requests(prob, layers, pools, step_ms, dec_ms, clock, args):
     """The same draft-verify step done by a decode that takes one query row
     per request: each of the R rows of request b becomes a request of its own
     over the first L_b - (R - 1 - r) tokens (same page-table row, same KV
@@ -605,10 +702,11 @@ def rows_as_requests(prob, layers, pools, step_ms, dec_ms, capture, graph_avg_ms
             run.combine()
 
     step()
-    warm = min(WARM_GPU_MS, args.warm_ms)   # warmed like the step and decode it is set against
-    per = graph_avg_ms(step, 1, reps=max(2, min(10, args.steps)), warm=warm)
+    warm = clock.warm_later   # warmed like the step and decode it is set against
+    per = clock.graph_avg_ms(step, 1, reps=max(2, min(10, args.steps)), warm=warm)
     n_dec = max(layers, pools)
-    dec = graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec, warm=warm)
+    dec = clock.graph_avg_ms(lambda: [run.decode(i % pools) for i in range(n_dec)], n_dec,
+                             warm=warm)
     return {"rows": R,
             "rows_as_requests_us_per_step": round(per * 1e3, 1),
             "rows_as_requests_decode_avg_us": round(dec * 1e3, 2),
@@ -616,34 +714,29 @@ def rows_as_requests(prob, layers, pools, step_ms, dec_ms, capture, graph_avg_ms
             "decode_speedup_vs_rows_as_requests": round(dec / dec_ms, 3)}
 
 
-def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8,
-                 warm_ms=WARM_GPU_MS):
+def static_sweep(run, prob, layers, pools, clock, reps=8):
     """Time the static split-KV baseline (decode + combine) at every sweep
-    point against dynamic decode + combine on the same pools, each as a HIP
-    graph of `reps` back-to-back calls rotating over the pools."""
+    point against dynamic decode + combine (two launches, and fused) on the
+    same pools, each as a HIP graph of `reps` back-to-back calls rotating
+    over the pools, replayed untimed for the warm time first."""
     import torch
 
     def timed(fn):
         fn(0)                       # allocates the sweep point's buffers
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in range(reps):
-                fn((r + 1) % pools)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        g = clock.capture(lambda: [fn((r + 1) % pools) for r in range(reps)])
+        a, b = clock.events()
+        a.record(clock.stream)
         g.replay()
-        b.record(stream)
+        b.record(clock.stream)
         b.synchronize()
-        # untimed replays first, as for the step: at least WARM_GPU_MS of GPU time
-        for _ in range(math.ceil(warm_ms / max(a.elapsed_time(b), 1e-3))):
+        for _ in range(math.ceil(clock.warm_later / max(a.elapsed_time(b), 1e-3))):
             g.replay()
         torch.cuda.synchronize()
-        a.record(stream)
+        a.record(clock.stream)
         for _ in range(5):
             g.replay()
-        b.record(stream)
+        b.record(clock.stream)
         b.synchronize()
         return a.elapsed_time(b) / (5 * reps) * 1e3
 
@@ -651,14 +744,22 @@ def static_sweep(run, prob, layers, pools, stream, dyn_decode_ms, reps=8,
         run.decode(pool)
         run.combine()
 
-    res = {"dynamic_us": round(timed(dyn), 2), "static_us": {}}
+    run.plan()   # one map for every replay (the plan's cost is not in either side)
+    torch.cuda.synchronize()
+    res = {"dynamic_us": round(timed(dyn), 2),
+           "dynamic_fused_us": round(timed(lambda p: run.decode_combine(p)), 2),
+           "static_us": {}}
     for S in (1, 2, 4, 8, 16, 32, 64, 128):
         res["static_us"]["splits=%d" % S] = round(timed(lambda p: run.static(0, S, p)), 2)
     for C in (256, 512, 1024, 2048, 4096, 8192):
         res["static_us"]["chunk=%d" % C] = round(timed(lambda p: run.static(1, C, p)), 2)
+    run.release_static()
     best = min(res["static_us"], key=res["static_us"].get)
     res["best_static"] = best
+    res["best_static_us"] = res["static_us"][best]
     res["speedup_vs_best_static"] = round(res["static_us"][best] / res["dynamic_us"], 3)
+    res["fused_speedup_vs_best_static"] = round(res["static_us"][best] / res["dynamic_fused_us"],
+                                                3)
     return res
 
 

@@ -751,12 +751,34 @@ __device__ __forceinline__ void merge_segment(const DecodeParams &p, int b, int 
 
 // After a workgroup wrote the partial of its descriptor in segment (b, h)
 // (all threads): take a ticket; the last one merges.  `last` is LDS.
+//
+// Why the last workgroup sees every partial, on a chip whose 8 XCDs each
+// have an L2 that is not coherent with the others, without the release /
+// acquire fences of the language (each would write back or invalidate a
+// whole L2):
+//   1. every partial row and LSE is stored with the sc1 cache policy
+//      (publish4 / publish), which writes through the XCD's L2 to the
+//      device-coherent level;
+//   2. each wave waits until its stores are acknowledged (s_waitcnt
+//      vmcnt(0): on gfx950 stores count in vmcnt, and an sc1 store is
+//      acknowledged once it is device-coherent), then the barrier orders
+//      all waves of the workgroup before the ticket;
+//   3. the ticket is an agent-scope atomic, performed at the device-coherent
+//      level, so every workgroup's increment is ordered after its own
+//      partials became device-coherent;
+//   4. the workgroup that takes the last ticket loads the partials with sc1
+//      (fetch4 / fetch): they miss its own L2 and read the device-coherent
+//      copies.  Those loads are issued only after the atomic returned and
+//      the barrier that broadcasts `last`, so none can precede it.
+// The reset is an agent-scope atomic store too, so the next launch (or the
+// next call on the same tickets) reads zero without relying on the L2
+// write-back at the end of this kernel.
 template <int D>
 __device__ __forceinline__ void ticket_and_merge(const DecodeParams &p, int b, int h,
                                                  int64_t k0, int n, int &last, int nthreads) {
     const int s = b * p.Hkv + h;
-    // Every wave's partial stores (agent-scope atomics) have completed
-    // (s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)) before the ticket is taken.
+    // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): this wave's partial stores
+    // are device-coherent before the barrier and the ticket.
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (threadIdx.x == 0)
@@ -765,7 +787,8 @@ __device__ __forceinline__ void ticket_and_merge(const DecodeParams &p, int b, i
     __syncthreads();
     if (last) {
         merge_segment<D>(p, b, h, k0, n, nthreads);
-        if (threadIdx.x == 0) p.tickets[s] = 0;
+        if (threadIdx.x == 0)
+            __hip_atomic_store(p.tickets + s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1500,8 +1523,8 @@ static_decode_kernel(DecodeParams p) {
 
 // Shared-tile kernels (2 .. 4 column blocks): NCB compute waves per
 // workgroup, plus a staging wave when SW, sized for three waves per SIMD;
-// the bf16 instance with two column blocks and no staging wave needs 176
-// registers and runs at two.
+// the bf16 instance with two column blocks and no staging wave needs 190
+// registers (hipcc -O3 for gfx950) and runs at two.
 template <class KV, int D, int NCB, int SW>
 constexpr int shared_waves_per_eu() {
     return (!KV::kScaled && D == 128 && NCB == 2 && SW == 0) ? 2 : 3;

@@ -191,9 +191,11 @@ def hpcattn_version() -> int:
 
 
 def alloc_task_map(batch: int, num_kv_heads: int, num_bins: int, device) -> TaskMap:
+    """A zeroed task-map buffer: until hpcattn_plan writes it, every bin is
+    empty, so a decode on it does no work (and reads no descriptor)."""
     import torch
     n = hpcattn_task_map_bytes(batch, num_kv_heads, num_bins) // 4
-    return TaskMap(torch.empty(n, dtype=torch.int32, device=device), batch, num_kv_heads,
+    return TaskMap(torch.zeros(n, dtype=torch.int32, device=device), batch, num_kv_heads,
                    num_bins)
 
 

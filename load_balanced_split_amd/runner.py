@@ -100,6 +100,10 @@ class DecodeRunner:
                 max_len)
         return self._static[key]
 
+    def release_static(self):
+        """Drop the static sweep's partial buffers."""
+        self._static.clear()
+
     def static(self, policy: int, param: int, layer: int = 0, stream=None):
         """Static split-KV decode + combine; returns (out, out_lse)."""
         po, pl, max_len = self.static_buffers(policy, param)

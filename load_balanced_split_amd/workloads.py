@@ -53,6 +53,14 @@ def _heavy_tail(rng, order: str = "random"):
     return lens[rng.permutation(lens.shape[0])].astype(np.int32)
 
 
+def _heavy_tail_long_first(rng):
+    return _heavy_tail(rng, "long_first")
+
+
+def _heavy_tail_long_last(rng):
+    return _heavy_tail(rng, "long_last")
+
+
 def _fp8(rng):
     return _log_uniform(rng, 32, 1024, 131072)
 
@@ -87,11 +95,22 @@ WORKLOADS: Dict[str, Workload] = {
     "single_long": Workload("single_long", _single_long, 8, 64, 128, "bf16"),
     "mixed": Workload("mixed", _mixed, 8, 64, 128, "bf16", layers=32),
     "heavy_tail": Workload("heavy_tail", _heavy_tail, 8, 64, 128, "bf16"),
+    # The same lengths with the 8 long requests first, or last, in the batch
+    # (order checks: a static grid dispatches its long workgroups first or
+    # last; the dynamic bins do not depend on the order).
+    "heavy_tail_long_first": Workload("heavy_tail_long_first", _heavy_tail_long_first, 8, 64,
+                                      128, "bf16"),
+    "heavy_tail_long_last": Workload("heavy_tail_long_last", _heavy_tail_long_last, 8, 64, 128,
+                                     "bf16"),
     "fp8": Workload("fp8", _fp8, 8, 64, 128, "fp8"),
     # A draft-verify step ("SGLang Low-Latency Mode", section 1: the confirmed
     # token and five drafts per request, six rows) over the mixed length mix.
     "mtp": Workload("mtp", _mixed, 8, 64, 128, "bf16", layers=32, q_rows=6),
     "mtp_fp8": Workload("mtp_fp8", _fp8, 8, 64, 128, "fp8", q_rows=6),
+    # One GPU's share of the mixed batch when the heads are split over 8 GPUs
+    # ("HPC-Ops x SGLang", SGLang serving with tensor parallelism 8): 1 KV
+    # head and its 8 query heads per GPU, the same lengths, 32 layers.
+    "mixed_shard": Workload("mixed_shard", _mixed, 1, 8, 128, "bf16", layers=32),
 }
 
 
