@@ -82,7 +82,7 @@ typedef enum {
     HPCATTN_ERR_NULL = -1,      /* a required pointer is NULL                  */
     HPCATTN_ERR_SHAPE = -2,     /* a size is out of range or inconsistent      */
     HPCATTN_ERR_DTYPE = -3,     /* unknown dtype, or scales given/missing      */
-    HPCATTN_ERR_WORKSPACE = -4, /* a caller buffer is smaller than required    */
+    HPCATTN_ERR_WORKSPACE = -4, /* a buffer (caller's or fixed scratch) too small */
     HPCATTN_ERR_LAUNCH = -5,    /* the HIP runtime reported a launch error     */
     HPCATTN_ERR_ARG = -6        /* another argument is out of range            */
 } hpcattn_status;
@@ -244,6 +244,35 @@ int hpcattn_decode_combine(const hpcattn_dims *dims, const void *q, const float 
                            float *part_o, float *part_lse, int64_t part_o_rows,
                            int32_t *tickets, int64_t num_tickets, void *out,
                            float *out_lse, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same call
+ * as hpcattn_decode_combine, with the same result, whose partials and
+ * tickets live in a fixed scratch array that the library holds on each
+ * device it runs on, from the first call until the process ends.  The
+ * caller passes inputs, the task map and out / out_lse only.
+ *
+ * Limits: B * H_kv <= HPCATTN_NOALLOC_MAX_SEGMENTS, and the partials,
+ * hpcattn_max_partials(B, H_kv, P) rows of R G (D + 1) fp32 values (each
+ * block 256-byte aligned), fit in HPCATTN_NOALLOC_SCRATCH_BYTES after the
+ * ticket block; otherwise HPCATTN_ERR_WORKSPACE and nothing is enqueued.
+ * The call allocates and frees nothing.  Its first call on a device looks
+ * up that device's array and enqueues one small kernel that zeroes the
+ * tickets (static storage starts at zero too); every call leaves them zero.
+ * Every call on one device shares that device's array: calls that may
+ * overlap on one device (other streams, concurrent graphs) race and must be
+ * ordered by the caller.  Errors as for hpcattn_decode_combine, plus
+ * HPCATTN_ERR_LAUNCH when the runtime cannot name the array's address.
+ */
+#define HPCATTN_NOALLOC_SCRATCH_BYTES (32u << 20)   /* per device               */
+#define HPCATTN_NOALLOC_MAX_SEGMENTS 65536          /* B * H_kv                 */
+
+int hpcattn_decode_combine_noalloc(const hpcattn_dims *dims, const void *q, const float *q_scale,
+                                   const void *k_pages, const void *v_pages,
+                                   const float *k_scale, const float *v_scale,
+                                   const int32_t *page_table, const hpcattn_task_map *map,
+                                   void *out, float *out_lse, void *stream);
 
 /*
  * Static split-KV decode, the scheme the dynamic one replaces ("Attention:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhpcattn.so")
 SOURCES = ["plan.hip", "decode.hip", "combine.hip", "probe.hip", "prologue.hip", "api.cpp",
-           "validate.cpp"]
+           "validate.cpp", "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions (v_pk_*_f32) stay off: plain fp32 code only.

@@ -188,6 +188,34 @@ bool fuse_combine(const hpcattn_dims *d, const hpcattn_task_map *map) {
     return mean_chunks < 8 && rows <= 16;
 }
 
+static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+ScratchPlan scratch_plan(const hpcattn_dims *d, const hpcattn_task_map *map) {
+    ScratchPlan s{};
+    const int64_t rg = (int64_t)d->q_rows * (d->num_q_heads / d->num_kv_heads);
+    s.num_tickets = (int64_t)map->batch * map->num_kv_heads;
+    s.rows = hpcattn_max_partials(map->batch, map->num_kv_heads, map->num_bins);
+    s.lse = align256(4 * (int64_t)HPCATTN_NOALLOC_MAX_SEGMENTS);
+    s.o = s.lse + align256(4 * s.rows * rg);
+    s.end = s.o + 4 * s.rows * rg * d->head_dim;
+    return s;
+}
+
+int check_decode_combine_noalloc(const hpcattn_dims *d, const void *q, const float *q_scale,
+                                 const void *k_pages, const void *v_pages, const float *k_scale,
+                                 const float *v_scale, const int32_t *page_table,
+                                 const hpcattn_task_map *map, const void *out) {
+    const int rc = check_decode_inputs(d, q, q_scale, k_pages, v_pages, k_scale, v_scale,
+                                       page_table, map);
+    if (rc) return rc;
+    if (!out) return HPCATTN_ERR_NULL;
+    const ScratchPlan s = scratch_plan(d, map);
+    if (s.num_tickets > HPCATTN_NOALLOC_MAX_SEGMENTS ||
+        s.end > (int64_t)HPCATTN_NOALLOC_SCRATCH_BYTES)
+        return HPCATTN_ERR_WORKSPACE;
+    return HPCATTN_OK;
+}
+
 }  // namespace hpcattn
 
 extern "C" {
@@ -217,7 +245,8 @@ const char *hpcattn_strerror(int status) {
     case HPCATTN_ERR_NULL: return "a required pointer is NULL";
     case HPCATTN_ERR_SHAPE: return "a size is out of range or inconsistent";
     case HPCATTN_ERR_DTYPE: return "unknown KV dtype, or scales given for bf16 / missing for fp8";
-    case HPCATTN_ERR_WORKSPACE: return "a caller buffer is smaller than required";
+    case HPCATTN_ERR_WORKSPACE:
+        return "a caller buffer (or the fixed scratch of the allocation-free call) is too small";
     case HPCATTN_ERR_LAUNCH: return "the HIP runtime reported a launch error";
     case HPCATTN_ERR_ARG: return "an argument is out of range";
     default: return "unknown status";

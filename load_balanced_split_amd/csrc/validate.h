@@ -55,4 +55,23 @@ int check_prologue(const hpcattn_prologue_dims *d, const void *qkv, const int32_
 // as decode, then combine).
 bool fuse_combine(const hpcattn_dims *d, const hpcattn_task_map *map);
 
+// Byte offsets of the allocation-free entry point's buffers inside its
+// fixed scratch array: the tickets always at 0, HPCATTN_NOALLOC_MAX_SEGMENTS
+// int32 (fixed, so that one call's partials never lie where a later call's
+// tickets are expected to be zero); part_lse [rows, R G] fp32 at `lse`;
+// part_o [rows, R G, D] fp32 at `o`, 256-byte aligned; `end` is the bytes used.
+struct ScratchPlan {
+    int64_t num_tickets, rows;
+    int64_t lse, o, end;
+};
+ScratchPlan scratch_plan(const hpcattn_dims *d, const hpcattn_task_map *map);
+
+// The checks of hpcattn_decode_combine_noalloc: those of decode_combine for
+// the buffers the caller passes, then HPCATTN_ERR_WORKSPACE when the batch
+// has more segments than tickets or the partials need more than the array.
+int check_decode_combine_noalloc(const hpcattn_dims *d, const void *q, const float *q_scale,
+                                 const void *k_pages, const void *v_pages, const float *k_scale,
+                                 const float *v_scale, const int32_t *page_table,
+                                 const hpcattn_task_map *map, const void *out);
+
 }  // namespace hpcattn

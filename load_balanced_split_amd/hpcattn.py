@@ -30,6 +30,8 @@ KV_FP8_E4M3 = 1
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
 MAPERR_NEG_LEN, MAPERR_OVERFLOW = 1, 2
+NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_MAX_SEGMENTS = 65536
 
 
 class hpcattn_dims(ctypes.Structure):
@@ -89,6 +91,10 @@ _sig = {
     "hpcattn_decode_combine": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims), _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, ctypes.POINTER(hpcattn_task_map),
                                               _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "hpcattn_decode_combine_noalloc": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims), _vp, _vp,
+                                                      _vp, _vp, _vp, _vp, _vp,
+                                                      ctypes.POINTER(hpcattn_task_map), _vp,
+                                                      _vp, _vp]),
     "hpcattn_combine": (ctypes.c_int, [ctypes.POINTER(hpcattn_dims),
                                        ctypes.POINTER(hpcattn_task_map), _vp, _vp, _vp, _vp,
                                        _vp]),
@@ -232,6 +238,19 @@ def hpcattn_decode_combine(dims: hpcattn_dims, q, k_pages, v_pages, page_table,
                                        _ptr(part_lse), rows, _ptr(tickets), nt, _ptr(out),
                                        _ptr(out_lse), _stream(stream)),
            "hpcattn_decode_combine")
+
+
+def hpcattn_decode_combine_noalloc(dims: hpcattn_dims, q, k_pages, v_pages, page_table,
+                                   task_map: TaskMap, out, out_lse=None, q_scale=None,
+                                   k_scale=None, v_scale=None, stream=None) -> None:
+    """Decode + combine with the partials and tickets in the library's fixed
+    per-device scratch: the caller passes no workspace."""
+    _check(_lib.hpcattn_decode_combine_noalloc(ctypes.byref(dims), _ptr(q), _ptr(q_scale),
+                                               _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                               _ptr(v_scale), _ptr(page_table),
+                                               ctypes.byref(task_map.handle), _ptr(out),
+                                               _ptr(out_lse), _stream(stream)),
+           "hpcattn_decode_combine_noalloc")
 
 
 def hpcattn_combine(dims: hpcattn_dims, task_map: TaskMap, part_o, part_lse, out,

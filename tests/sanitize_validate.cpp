@@ -160,6 +160,34 @@ static void test_decode_paths() {
     EXPECT(fuse_combine(&d1, &many), false);
 }
 
+static void test_noalloc() {
+    hpcattn_dims d = dims();
+    hpcattn_task_map m = map_for(4, 1, 8);
+    EXPECT(check_decode_combine_noalloc(&d, F, nullptr, F, F, nullptr, nullptr, FI, &m, F),
+           HPCATTN_OK);
+    EXPECT(check_decode_combine_noalloc(&d, F, nullptr, F, F, nullptr, nullptr, FI, &m, nullptr),
+           HPCATTN_ERR_NULL);
+    const ScratchPlan s = scratch_plan(&d, &m);
+    EXPECT(s.lse, 4 * HPCATTN_NOALLOC_MAX_SEGMENTS);   // tickets first, at a fixed size
+    EXPECT(s.o % 256, 0);
+    EXPECT(s.end, s.o + 4 * s.rows * 4 * 64);
+    // 8192 x 2 segments of 8 rows at D = 128: partials past the array
+    hpcattn_dims big = dims(HPCATTN_MAX_BATCH, 16, 2, 128);
+    hpcattn_task_map mb = map_for(HPCATTN_MAX_BATCH, 2, 512);
+    EXPECT(check_decode_combine_noalloc(&big, F, nullptr, F, F, nullptr, nullptr, FI, &mb, F),
+           HPCATTN_ERR_WORKSPACE);
+    // more segments than tickets, however small the partials
+    hpcattn_dims wide = dims(HPCATTN_MAX_BATCH, 9, 9, 64);
+    hpcattn_task_map mw = map_for(HPCATTN_MAX_BATCH, 9, 1);
+    EXPECT(check_decode_combine_noalloc(&wide, F, nullptr, F, F, nullptr, nullptr, FI, &mw, F),
+           HPCATTN_ERR_WORKSPACE);
+    // the largest map the checks admit: no overflow in the plan's products
+    hpcattn_dims huge = dims(HPCATTN_MAX_BATCH, 16, 1, 128, 4);
+    hpcattn_task_map mh = map_for(HPCATTN_MAX_BATCH, 1, I32MAX - HPCATTN_MAX_BATCH + 1);
+    EXPECT(check_decode_combine_noalloc(&huge, F, nullptr, F, F, nullptr, nullptr, FI, &mh, F),
+           HPCATTN_ERR_WORKSPACE);
+}
+
 static void test_static() {
     hpcattn_dims d = dims();
     float *po = (float *)F;
@@ -245,6 +273,7 @@ int main() {
     test_map_and_plan();
     test_decode_paths();
     test_static();
+    test_noalloc();
     test_probe_and_prologue();
     for (int s = -8; s <= 1; ++s)
         if (!hpcattn_strerror(s)) ++failures;

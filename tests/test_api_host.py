@@ -137,6 +137,30 @@ def test_decode_combine_rejects_bad_arguments(H):
     assert dc(_dims(H, kv_dtype=H.KV_FP8_E4M3)) == H.ERR_DTYPE
 
 
+def test_noalloc_rejects_bad_arguments_and_oversized_problems(H):
+    lib = H._lib
+
+    def na(dims, mp, out=FAKE, ptrs=FAKE):
+        return lib.hpcattn_decode_combine_noalloc(ctypes.byref(dims), ptrs, None, ptrs, ptrs,
+                                                  None, None, ptrs, ctypes.byref(mp), out, None,
+                                                  None)
+
+    m = _map(H)
+    assert na(_dims(H), m, out=None) == H.ERR_NULL
+    assert na(_dims(H), m, ptrs=None) == H.ERR_NULL
+    assert na(_dims(H, batch=5), m) == H.ERR_SHAPE
+    assert na(_dims(H, kv_dtype=H.KV_FP8_E4M3), m) == H.ERR_DTYPE
+    assert na(_dims(H), _map(H, nbytes=16)) == H.ERR_WORKSPACE
+    # partials of 8192 x 2 segments + 511 bins, 8 rows of D = 128: 67 MB > 32 MiB
+    big = H.hpcattn_task_map(FAKE, H.hpcattn_task_map_bytes(8192, 2, 512), 8192, 2, 512, 1)
+    assert na(_dims(H, batch=8192, num_q_heads=16, num_kv_heads=2, head_dim=128), big) == \
+        H.ERR_WORKSPACE
+    # more segments than tickets
+    many = H.hpcattn_task_map(FAKE, H.hpcattn_task_map_bytes(8192, 9, 1), 8192, 9, 1, 1)
+    assert na(_dims(H, batch=8192, num_q_heads=9, num_kv_heads=9, head_dim=64), many) == \
+        H.ERR_WORKSPACE
+
+
 def test_combine_and_static_reject_bad_arguments(H):
     lib = H._lib
     m = _map(H)
