@@ -320,6 +320,11 @@ int64_t hpcattn_static_max_partials(int32_t batch, int32_t num_kv_heads, int32_t
 int hpcattn_probe_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
                               uint32_t *sink, void *stream);
 
+/* Prologue limits: H_q + 2 H_kv heads at most, and T * 64 * min(ceil((H_q +
+ * 2 H_kv) / 16), 16) below 2^32 (one workgroup per token with one wave per
+ * 16 heads; at 256 heads or more, T below 4194304). */
+#define HPCATTN_PROLOGUE_MAX_HEADS 65536
+
 /* Prologue flags. */
 #define HPCATTN_PROLOGUE_ROPE 1      /* rotate Q and K by their positions      */
 #define HPCATTN_PROLOGUE_HADAMARD 2  /* rotate Q and K by H_D / sqrt(D)         */
@@ -360,8 +365,8 @@ typedef struct {
  * q_norm_w, k_norm_w  device fp32 [D] or NULL (no QK-Norm)
  * q_scale, k_scale, v_scale: required for fp8, NULL for bf16.
  * Writes only q_out/q_scale rows of the T tokens and the cache rows named by
- * cache_slots.  Errors: NULL pointers, sizes out of range, unknown flags or
- * dtype, eps < 0, rope_base <= 0.
+ * cache_slots.  Errors: NULL pointers, sizes out of range (see the
+ * prologue limits above), unknown flags or dtype, eps < 0, rope_base <= 0.
  */
 int hpcattn_prologue(const hpcattn_prologue_dims *dims, const void *qkv,
                      const int32_t *positions, const int32_t *cache_slots,

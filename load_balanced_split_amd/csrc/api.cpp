@@ -204,7 +204,8 @@ int hpcattn_prologue(const hpcattn_prologue_dims *d, const void *qkv, const int3
     p.kv_dtype = d->kv_dtype;
     p.flags = d->flags;
     p.eps = d->eps;
-    p.log2_base = std::log2((double)d->rope_base);
+    for (int i = 0; i < d->head_dim / 2; ++i)
+        p.freq[i] = std::pow((double)d->rope_base, -2.0 * i / d->head_dim);
     return launch_status(launch_prologue(p, d->head_dim, (hipStream_t)stream));
 }
 

@@ -67,9 +67,8 @@ struct PrologueParams {
     float *k_scale;
     float *v_scale;
     int32_t T, Hq, Hkv, num_pages, kv_dtype, flags;
-    int32_t chunks;     // groups of 4 heads per wave (set by the launcher)
     float eps;
-    double log2_base;   // log2 of the RoPE base
+    double freq[64];            // RoPE frequencies base^(-2i/D), i < D/2
 };
 
 hipError_t launch_plan(const int32_t *seq_lens, int32_t B, int32_t Hkv, int32_t P,

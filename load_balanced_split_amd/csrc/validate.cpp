@@ -2,6 +2,8 @@
 // (sizes, status strings, version).  No HIP here: see validate.h.
 #include "validate.h"
 
+#include <algorithm>
+
 #include <math.h>
 
 #include "layout.h"
@@ -159,9 +161,13 @@ int check_prologue(const hpcattn_prologue_dims *d, const void *qkv, const int32_
                    const float *v_scale) {
     if (!d) return HPCATTN_ERR_NULL;
     if (d->num_tokens < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
-        (d->head_dim != 64 && d->head_dim != 128) || d->num_pages < 1 ||
-        (int64_t)d->num_tokens * ((int64_t)d->num_q_heads + 2 * (int64_t)d->num_kv_heads) >
-            INT32_MAX * 4ll)
+        (d->head_dim != 64 && d->head_dim != 128) || d->num_pages < 1)
+        return HPCATTN_ERR_SHAPE;
+    // The launch: one workgroup per token with one wave per 16 heads (at most
+    // 16 waves); a grid's extent in work-items is 32-bit.
+    const int64_t heads = (int64_t)d->num_q_heads + 2 * (int64_t)d->num_kv_heads;
+    const int64_t waves = std::min<int64_t>((heads + 15) / 16, 16);
+    if (heads > HPCATTN_PROLOGUE_MAX_HEADS || (int64_t)d->num_tokens * 64 * waves > UINT32_MAX)
         return HPCATTN_ERR_SHAPE;
     if (d->kv_dtype != HPCATTN_KV_BF16 && d->kv_dtype != HPCATTN_KV_FP8_E4M3)
         return HPCATTN_ERR_DTYPE;

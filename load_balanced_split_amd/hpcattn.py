@@ -49,6 +49,7 @@ class hpcattn_dims(ctypes.Structure):
 
 
 PROLOGUE_ROPE, PROLOGUE_HADAMARD = 1, 2
+PROLOGUE_MAX_HEADS = 65536
 
 
 class hpcattn_prologue_dims(ctypes.Structure):

@@ -249,12 +249,17 @@ static void test_probe_and_prologue() {
     q.num_q_heads = I32MAX;
     q.num_kv_heads = I32MAX;
     EXPECT(check_prologue(&q, F, FI, FI, F, nullptr, F, F, nullptr, nullptr), HPCATTN_ERR_SHAPE);
-    q = p;
-    q.num_tokens = I32MAX;   // 12 rows per token: past 4 (2^31 - 1) rows
+    q = p;   // 12 heads: one wave per token, T * 64 work-items below 2^32
+    q.num_tokens = I32MAX;
     EXPECT(check_prologue(&q, F, FI, FI, F, nullptr, F, F, nullptr, nullptr), HPCATTN_ERR_SHAPE);
-    q.num_tokens = I32MAX / 4;
+    q.num_tokens = 1 << 26;
+    EXPECT(check_prologue(&q, F, FI, FI, F, nullptr, F, F, nullptr, nullptr), HPCATTN_ERR_SHAPE);
+    q.num_tokens = (1 << 26) - 1;
     EXPECT(check_prologue(&q, F, FI, FI, F, nullptr, F, F, nullptr, nullptr), HPCATTN_OK);
-    q.num_q_heads = 1 << 20;
+    q.num_tokens = 4;
+    q.num_q_heads = HPCATTN_PROLOGUE_MAX_HEADS - 4;   // heads = the maximum
+    EXPECT(check_prologue(&q, F, FI, FI, F, nullptr, F, F, nullptr, nullptr), HPCATTN_OK);
+    q.num_q_heads += 1;
     EXPECT(check_prologue(&q, F, FI, FI, F, nullptr, F, F, nullptr, nullptr), HPCATTN_ERR_SHAPE);
     q = p;
     q.eps = std::numeric_limits<float>::quiet_NaN();

@@ -225,8 +225,33 @@ def test_prologue_rejects_bad_arguments(H):
     assert lib.hpcattn_prologue(ctypes.byref(big), FAKE, FAKE, FAKE, None, None, FAKE, None,
                                 FAKE, FAKE, None, None, None) == H.ERR_SHAPE
 
+    def shape(T, Hq, Hkv):
+        d = H.hpcattn_prologue_dims(T, Hq, Hkv, 128, 4, H.KV_BF16, 1, 1e-6, 1e4)
+        return lib.hpcattn_prologue(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                    FAKE, FAKE, None, None, None)
+    # one token with more heads than the kernel indexes in int32
+    assert shape(1, 2 ** 31 - 1, 1) == H.ERR_SHAPE
+    assert shape(1, H.PROLOGUE_MAX_HEADS - 1, 1) == H.ERR_SHAPE
+    # the grid's extent: T * 64 * min(ceil(heads / 16), 16) work-items below 2^32
+    assert shape(2 ** 22, 240, 8) == H.ERR_SHAPE         # 256 heads: 16 waves per token
+    assert shape(13421773, 64, 8) == H.ERR_SHAPE         # 80 heads: 5 waves per token
+
 
 def test_strerror_covers_every_status(H):
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert H.hpcattn_strerror(code) != "unknown status"
     assert H.hpcattn_strerror(-99) == "unknown status"
+
+
+
+def test_binding_constants_match_the_header(H):
+    """Every integer #define of include/hpcattn.h (HPCATTN_X) that the Python
+    binding mirrors as X has the same value there."""
+    text = open(os.path.join(ROOT, "include", "hpcattn.h")).read()
+    seen = 0
+    for m in re.finditer(r"^#define HPCATTN_(\w+) +([^/\n]+?)\s*(?:/\*.*)?$", text, re.M):
+        name, expr = m.group(1), re.sub(r"(\d+)u\b", r"\1", m.group(2))
+        if re.fullmatch(r"[\d()< ]+", expr) and hasattr(H, name):
+            assert getattr(H, name) == eval(expr), name
+            seen += 1
+    assert seen >= 8, seen

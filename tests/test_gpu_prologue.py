@@ -92,7 +92,9 @@ def check_codes(got, ref, val, scale, what):
 CASES = [  # (T, Hq, Hkv, D, flags)
     (64, 8, 1, 128, 1), (64, 64, 8, 128, 1), (37, 4, 2, 64, 1), (50, 8, 2, 128, 3),
     (16, 4, 4, 64, 3), (33, 16, 2, 128, 0), (1, 2, 1, 64, 2),
-    (1100, 16, 2, 128, 3), (1030, 8, 8, 64, 1),     # >= 1024 tokens: one workgroup per token
+    (1100, 16, 2, 128, 3), (1030, 8, 8, 64, 1),
+    # large calls: thousands of workgroups, every flag path at D = 128 and 64
+    (4099, 64, 8, 128, 3), (9001, 32, 8, 64, 1),
 ]
 
 
