@@ -108,6 +108,10 @@ def parse_args():
                          "from a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--oracle-layer", action="store_true",
+                    help="instead of the benchmark: time the fp64 CPU oracle on one full layer "
+                         "of the workload (all host cores, then 1 thread; median of 3 each), "
+                         "print one JSON line; needs no GPU")
     ap.add_argument("--calibrate", action="store_true",
                     help="instead of the benchmark: time a plain 1 GiB device copy and a "
                          "4 GiB read-reduce (HBM read probe), print one JSON line")
@@ -163,6 +167,61 @@ def calibrate():
         "stream_read_GBs_by_loads_workgroups": probe, "stream_read_best_GBs": probe[best],
         "stream_read_best": best, "chunked_16k_read_GBs_by_workgroups": chunked,
         "chunked_16k_read_best_GBs": max(chunked.values())}), flush=True)
+
+
+def oracle_layer(name: str, seed: int, runs: int = 3):
+    """The fp64 oracle, as it stands, on one whole layer of a workload: every
+    (request, KV head) pair, on all host cores and then on one thread, the
+    median of `runs` passes each.  Inputs are built on the host."""
+    import numpy as np
+
+    import oracle
+    from load_balanced_split_amd import workloads as wl
+
+    prob = wl.make_problem(name, seed=seed, device="cpu", layers=1)
+    w = prob.workload
+    h = dict(q=wl.as_numpy(prob.q), k_pages=wl.as_numpy(prob.k_pages[0]),
+             v_pages=wl.as_numpy(prob.v_pages[0]))
+    if w.kv_dtype == "fp8":
+        h.update(q_scale=wl.as_numpy(prob.q_scale), k_scale=wl.as_numpy(prob.k_scale[0]),
+                 v_scale=wl.as_numpy(prob.v_scale[0]))
+    kv = int(np.asarray(prob.seq_lens).sum()) * wl.kv_bytes_per_token(w)
+
+    def layer():
+        t0 = time.perf_counter()
+        oracle.attention(h["q"], h["k_pages"], h["v_pages"], prob.page_table, prob.seq_lens,
+                         num_kv_heads=w.num_kv_heads, sm_scale=prob.sm_scale,
+                         q_scale=h.get("q_scale"), k_scale=h.get("k_scale"),
+                         v_scale=h.get("v_scale"))
+        dt = time.perf_counter() - t0
+        note("oracle layer pass: %.2f s" % dt)
+        return dt
+
+    cores = oracle.max_threads()
+    note("oracle layer", name, "on", cores, "threads")
+    t_all = statistics.median(layer() for _ in range(runs))
+    oracle.set_threads(1)
+    try:
+        note("oracle layer", name, "on 1 thread")
+        t_one = statistics.median(layer() for _ in range(runs))
+    finally:
+        oracle.set_threads(cores)
+    print(json.dumps({"oracle_layer": DESCRIPTIONS.get(name, name), "workload": name,
+                      "kv_bytes": kv, "runs": runs, "cores": cores,
+                      "us_all_cores": round(t_all * 1e6), "gbs_all_cores": round(kv / t_all / 1e9, 3),
+                      "us_one_thread": round(t_one * 1e6), "gbs_one_thread": round(kv / t_one / 1e9, 3),
+                      "host": _cpu_model()}), flush=True)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def prologue_bench(reps=20):
@@ -642,6 +701,9 @@ def main():
     args = parse_args()
     if args.calibrate:
         calibrate()
+        return
+    if args.oracle_layer:
+        oracle_layer(args.workload, args.seed)
         return
     if args.workload == "prologue":
         prologue_bench()
