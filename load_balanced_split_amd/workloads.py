@@ -109,8 +109,10 @@ WORKLOADS: Dict[str, Workload] = {
     "mtp_fp8": Workload("mtp_fp8", _fp8, 8, 64, 128, "fp8", q_rows=6),
     # One GPU's share of the mixed batch when the heads are split over 8 GPUs
     # ("HPC-Ops x SGLang", SGLang serving with tensor parallelism 8): 1 KV
-    # head and its 8 query heads per GPU, the same lengths, 32 layers.
-    "mixed_shard": Workload("mixed_shard", _mixed, 1, 8, 128, "bf16", layers=32),
+    # head and its 8 query heads per GPU, the same lengths, 32 layers.  Its
+    # ~6.6K tiles would make only ~206 bins of the 32-tile floor, fewer than
+    # the CUs; a floor of 8 tiles gives the 512 bins of the full batch.
+    "mixed_shard": Workload("mixed_shard", _mixed, 1, 8, 128, "bf16", layers=32, min_tiles=8),
 }
 
 
