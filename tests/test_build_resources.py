@@ -1,7 +1,7 @@
 """Build-time check of the decode kernels' resources (CPU; hipcc
 cross-compiles for gfx950 here).
 
-Every decode kernel is written to fit its register budget (the launch
+Every decode, combine and prologue kernel is written to fit its register budget (the launch
 bounds and waves-per-EU each kernel declares): a kernel that spilled would
 stream its spills through scratch memory: extra vector-memory operations
 and HBM traffic inside the KV loop, which is bound by its KV loads.  Checked in the
@@ -41,7 +41,8 @@ def _descriptors(asm):
     return res
 
 
-@pytest.mark.parametrize("source,at_least", [("decode.hip", 48), ("combine.hip", 2)])
+@pytest.mark.parametrize("source,at_least", [("decode.hip", 48), ("combine.hip", 2),
+                                             ("prologue.hip", 16)])
 def test_kernels_do_not_spill(tmp_path, source, at_least):
     asm = _asm(tmp_path, source)
     kernels = _descriptors(asm)
