@@ -95,6 +95,8 @@ CASES = [  # (T, Hq, Hkv, D, flags)
     (1100, 16, 2, 128, 3), (1030, 8, 8, 64, 1),
     # large calls: thousands of workgroups, every flag path at D = 128 and 64
     (4099, 64, 8, 128, 3), (9001, 32, 8, 64, 1),
+    # more than 256 heads: a token takes several workgroups of 16 waves
+    (5, 256, 8, 128, 3), (3, 300, 2, 64, 1),
 ]
 
 
