@@ -66,3 +66,15 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_oracle_layer_times_a_whole_layer(capsys):
+    """--oracle-layer: the oracle over every (request, KV head) pair of one
+    layer, all threads and one thread, one JSON line; no GPU involved."""
+    import json
+    bench.oracle_layer("tiny", 0, runs=1)
+    line = [x for x in capsys.readouterr().out.splitlines() if x.startswith("{")][-1]
+    d = json.loads(line)
+    assert d["workload"] == "tiny" and d["runs"] == 1 and d["cores"] >= 1
+    assert d["kv_bytes"] == 1281 * 256          # the tiny lengths, 1 KV head, D 64, bf16
+    assert d["us_all_cores"] > 0 and d["us_one_thread"] > 0
