@@ -103,12 +103,29 @@ CASES = [  # (T, Hq, Hkv, D, flags)
 @pytest.mark.parametrize("T,Hq,Hkv,D,flags", CASES)
 @pytest.mark.parametrize("fp8", [False, True])
 def test_prologue_matches_oracle(H, T, Hq, Hkv, D, flags, fp8):
+    check_against_oracle(H, T, Hq, Hkv, D, flags, fp8)
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D,flags,norm", [
+    (37, 8, 2, 128, 3, "none"), (20, 4, 4, 64, 1, "none"),
+    (37, 8, 2, 128, 3, "q only"), (29, 16, 2, 64, 2, "k only")])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prologue_without_norm_weights(H, T, Hq, Hkv, D, flags, norm, fp8):
+    """QK-Norm is skipped for a kind whose weights are NULL (no RMS factor)."""
+    check_against_oracle(H, T, Hq, Hkv, D, flags, fp8, use_qw=norm == "q only",
+                         use_kw=norm == "k only")
+
+
+def check_against_oracle(H, T, Hq, Hkv, D, flags, fp8, use_qw=True, use_kw=True):
     num_pages = max(2, (T + 63) // 64 + 3)
     qkv, pos, slots, qw, kw = make_inputs(T, Hq, Hkv, D, num_pages, seed=T * 31 + D + flags)
+    qw = qw if use_qw else None
+    kw = kw if use_kw else None
     q_out, kp, vp, sc = run_gpu(H, qkv, pos, slots, qw, kw, Hq, Hkv, D, num_pages, fp8, flags)
     ref = oracle.prologue(wl.as_numpy(qkv), pos.cpu().numpy(), num_q_heads=Hq,
-                          num_kv_heads=Hkv, head_dim=D, q_norm_w=qw.cpu().numpy(),
-                          k_norm_w=kw.cpu().numpy(), eps=1e-6,
+                          num_kv_heads=Hkv, head_dim=D,
+                          q_norm_w=None if qw is None else qw.cpu().numpy(),
+                          k_norm_w=None if kw is None else kw.cpu().numpy(), eps=1e-6,
                           rope=bool(flags & H.PROLOGUE_ROPE), rope_base=10000.0,
                           hadamard=bool(flags & H.PROLOGUE_HADAMARD))
     sl = slots.cpu().numpy()
