@@ -365,7 +365,8 @@ typedef struct {
  * q_norm_w, k_norm_w  device fp32 [D] or NULL (no QK-Norm)
  * q_scale, k_scale, v_scale: required for fp8, NULL for bf16.
  * Writes only q_out/q_scale rows of the T tokens and the cache rows named by
- * cache_slots.  Errors: NULL pointers, sizes out of range (see the
+ * cache_slots.  With T = 0 nothing is read or written and the buffer
+ * pointers may be NULL.  Errors: NULL pointers, sizes out of range (see the
  * prologue limits above), unknown flags or dtype, eps < 0, rope_base <= 0.
  */
 int hpcattn_prologue(const hpcattn_prologue_dims *dims, const void *qkv,

@@ -175,9 +175,10 @@ int check_prologue(const hpcattn_prologue_dims *d, const void *qkv, const int32_
         !(d->eps >= 0.f) || !isfinite(d->eps) || !(d->rope_base > 0.f) ||
         !isfinite(d->rope_base))
         return HPCATTN_ERR_ARG;
+    const bool fp8 = d->kv_dtype == HPCATTN_KV_FP8_E4M3;
+    if (d->num_tokens == 0) return HPCATTN_OK;   // nothing is read or written
     if (!qkv || !cache_slots || !q_out || !k_pages || !v_pages) return HPCATTN_ERR_NULL;
     if ((d->flags & HPCATTN_PROLOGUE_ROPE) && !positions) return HPCATTN_ERR_NULL;
-    const bool fp8 = d->kv_dtype == HPCATTN_KV_FP8_E4M3;
     if (fp8 ? !(q_scale && k_scale && v_scale) : (q_scale || k_scale || v_scale))
         return HPCATTN_ERR_DTYPE;
     return HPCATTN_OK;

@@ -245,6 +245,15 @@ static void test_probe_and_prologue() {
     EXPECT(check_prologue(&p, F, FI, FI, F, nullptr, F, F, nullptr, nullptr), HPCATTN_OK);
     EXPECT(check_prologue(&p, F, nullptr, FI, F, nullptr, F, F, nullptr, nullptr),
            HPCATTN_ERR_NULL);
+    {   // no tokens: nothing is touched, NULL buffers are fine (the other checks still hold)
+        hpcattn_prologue_dims z = p;
+        z.num_tokens = 0;
+        EXPECT(check_prologue(&z, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, nullptr), HPCATTN_OK);
+        z.head_dim = 96;
+        EXPECT(check_prologue(&z, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, nullptr), HPCATTN_ERR_SHAPE);
+    }
     hpcattn_prologue_dims q = p;   // H_q + 2 H_kv must not wrap in int32
     q.num_q_heads = I32MAX;
     q.num_kv_heads = I32MAX;

@@ -212,6 +212,9 @@ def test_prologue_rejects_bad_arguments(H):
                                 None, None, None) == H.ERR_NULL
     assert pro(D=96) == H.ERR_SHAPE
     assert pro(T=-1) == H.ERR_SHAPE
+    # no tokens: a no-op (no launch), NULL buffers accepted
+    assert pro(T=0, nulls=("qkv", "pos", "slots", "q", "k", "v")) == H.OK
+    assert pro(T=0, D=96) == H.ERR_SHAPE
     assert pro(flags=4) == H.ERR_ARG
     assert pro(eps=-1.0) == H.ERR_ARG
     assert pro(base=0.0) == H.ERR_ARG

@@ -212,3 +212,19 @@ def test_prologue_then_decode_end_to_end(H):
                                     v_scale=vs)
     rows = [(b, j) for b in range(B) for j in range(Hq)]
     compare(out, lse, ref_o, ref_l, rows, True, "prologue + decode (fp8)")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prologue_with_no_tokens_writes_nothing(H, fp8):
+    """T = 0 is a valid call that launches nothing: the cache keeps its bytes."""
+    Hq, Hkv, D, num_pages = 8, 2, 128, 2
+    qkv = torch.zeros((0, (Hq + 2 * Hkv) * D), dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    slots = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    q_out, kp, vp, sc = run_gpu(H, qkv, pos, slots, None, None, Hq, Hkv, D, num_pages, fp8, 3)
+    assert q_out.numel() == 0
+    if fp8:
+        assert (kp == 0x5A).all() and (vp == 0x5A).all()
+        assert (sc["k_scale"] == -1.0).all() and (sc["v_scale"] == -1.0).all()
+    else:
+        assert (kp.float() == 0.3125).all() and (vp.float() == 0.3125).all()
