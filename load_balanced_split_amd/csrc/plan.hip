@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kWaveChunks = 32;   // segments with more descriptors are written by a wave
+constexpr int kWideList = 64;     // such segments spread over all waves; more: their own wave
 
 struct Bins {
     int64_t T, P_eff, q, r;
@@ -85,7 +86,8 @@ plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_
             int32_t m, int32_t *__restrict__ map) {
     __shared__ int32_t s_cum[HPCATTN_MAX_BATCH + 1];   // tiles before request b; [B] = all
     __shared__ int64_t s_wave[kPlanWaves];
-    __shared__ int32_t s_err;
+    __shared__ int64_t s_wide[kWideList][7];   // b, h, st, en, j0, c, first descriptor
+    __shared__ int32_t s_err, s_nwide;
 
     const MapLayout lay(B, Hkv, P);
     int32_t *lens_out = map + lay.lens;
@@ -96,7 +98,10 @@ plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_
     const int64_t S = (int64_t)B * Hkv;
     const int64_t Dmax = S + P - 1;
 
-    if (tid == 0) s_err = 0;
+    if (tid == 0) {
+        s_err = 0;
+        s_nwide = 0;
+    }
     __syncthreads();
 
     // Phase A: tiles per request and their exclusive scan over requests.
@@ -160,9 +165,12 @@ plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_
     // Phase D: per-segment offsets and descriptors.  Each descriptor is the
     // intersection of segment s with one bin j; a bin's first descriptor also
     // sets its bin offset.  A thread writes the descriptors of its segment of
-    // the round; a segment of more than kWaveChunks (a single long request
-    // spans hundreds of bins) is written by the whole wave instead, a lane
-    // per descriptor, one such segment at a time.
+    // the round.  A segment of more than kWaveChunks (a long request spans
+    // hundreds of bins) is written by a whole wave, a lane per descriptor:
+    // the first kWideList such segments are listed in LDS and spread over all
+    // the waves afterwards (a few long requests would otherwise all fall to
+    // the waves that own them); any further ones by the wave that owns them,
+    // one at a time.
     auto put = [&](const Seg &g, int64_t i, int64_t d) {   // chunk i of g is descriptor d
         const int64_t j = g.j0 + i, bs = bins.start(j), be = bins.start(j + 1);
         const int64_t lo = bs > g.st ? bs : g.st, hi = be < g.en ? be : g.en;
@@ -184,7 +192,17 @@ plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_
         const bool wide = g.c > kWaveChunks;
         if (!wide)
             for (int64_t i = 0; i < g.c; ++i) put(g, i, run + i);
-        for (uint64_t longs = __ballot(wide); longs; longs &= longs - 1) {
+        bool listed = false;
+        if (wide) {
+            const int k = atomicAdd(&s_nwide, 1);
+            if (k < kWideList) {
+                const int64_t e[7] = {g.b, g.h, g.st, g.en, g.j0, g.c, run};
+#pragma unroll
+                for (int f = 0; f < 7; ++f) s_wide[k][f] = e[f];
+                listed = true;
+            }
+        }
+        for (uint64_t longs = __ballot(wide && !listed); longs; longs &= longs - 1) {
             const int l = __ffsll((unsigned long long)longs) - 1;   // wave-uniform
             Seg w;
             w.b = (int)lane_value(g.b, l);
@@ -199,6 +217,12 @@ plan_kernel(const int32_t *__restrict__ seq_lens, int32_t B, int32_t Hkv, int32_
         run += g.c;
     }
     if (tid == 0) seg_off[S] = (int32_t)num_desc;
+    __syncthreads();
+    for (int i = tid >> 6; i < min(s_nwide, kWideList); i += kPlanWaves) {   // wave-uniform i
+        const Seg w{(int)s_wide[i][0], (int)s_wide[i][1], s_wide[i][2],
+                    s_wide[i][3],      s_wide[i][4],      s_wide[i][5]};
+        for (int64_t k = lane; k < w.c; k += 64) put(w, k, s_wide[i][6] + k);
+    }
 
     // Phase E: bins that own no tile start at num_desc.
     for (int64_t j = tid; j <= P; j += kPlanThreads)
