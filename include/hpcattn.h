@@ -225,7 +225,8 @@ int hpcattn_combine(const hpcattn_dims *dims, const hpcattn_task_map *map,
  * hpcattn_combine does (up to summation order) and resets the ticket to 0.
  * No workgroup ever waits for another.  Where fusing does not pay -- a mean
  * of 8 or more chunks per segment (S + P - 1 descriptors over S = B H_kv
- * segments), or more than 16 query rows per KV head -- the call runs
+ * segments; 4 or more when q_rows * G > 16), or a shape whose fused kernel
+ * holds fewer workgroups per CU than hpcattn_decode's -- the call runs
  * hpcattn_decode and hpcattn_combine instead, with the same result.
  *
  * tickets: device int32 [num_tickets >= B * H_kv], all zero on entry; the

@@ -91,7 +91,9 @@ int hpcattn_decode_combine(const hpcattn_dims *dims, const void *q, const float 
                                  page_table, part_o, part_lse);
     p.map = map->words;
     p.P = map->num_bins;
-    if (!fuse_combine(dims, map)) {
+    const int32_t rows = dims->q_rows * (dims->num_q_heads / dims->num_kv_heads);
+    if (!fuse_combine(dims, map) ||
+        !fused_keeps_residency(dims->head_dim, dims->kv_dtype, rows)) {
         hipError_t e = launch_decode(p, dims->head_dim, dims->kv_dtype, (hipStream_t)stream);
         if (e != hipSuccess) return HPCATTN_ERR_LAUNCH;
         return hpcattn_combine(dims, map, part_o, part_lse, out, out_lse, stream);

@@ -81,6 +81,9 @@ hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 hipError_t launch_prologue(const PrologueParams &p, int32_t head_dim, hipStream_t stream);
 // rows = R * G, the query rows that share one KV head's tiles.
 int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t rows);
+// Whether the fused decode + combine instance for this shape holds as many
+// workgroups per CU as the decode alone (whose count sets the default bins).
+bool fused_keeps_residency(int32_t head_dim, int32_t kv_dtype, int32_t rows);
 hipError_t launch_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t flags,
                               uint32_t *sink, hipStream_t stream);
 

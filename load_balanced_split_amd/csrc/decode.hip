@@ -40,6 +40,8 @@
 //     the 4 waves are merged in LDS.
 // Scores are kept in log2 units (scaled by sm_scale * log2 e) and exp2 is
 // the hardware v_exp_f32; the stored LSE is natural-log.
+#include <atomic>
+
 #include "common.h"
 
 namespace hpcattn {
@@ -1108,6 +1110,7 @@ struct SharedLds {
     alignas(16) uint8_t kv[kTile * (kRow + kRowV)];   // K rows 0 .. 63, then V rows
     alignas(16) float ks[kTile];   // fp8 k and v scales of the tile's tokens
     alignas(16) float vs[kTile];
+    int last;   // the fused combine: this workgroup merges the segment
     __device__ const uint8_t *k() const { return kv; }
     __device__ const uint8_t *v() const { return kv + kTile * kRow; }
     __device__ uint8_t *v() { return kv + kTile * kRow; }
@@ -1273,25 +1276,74 @@ __device__ __forceinline__ void attend_shared(const DecodeParams &p, const Share
     }
 }
 
-// Normalise and write this wave's columns of partial slot `slot`.
-// The slot's rows start at a uniform address; the lane adds a 32-bit offset.
-template <int D>
+// Normalise and write this wave's columns of partial slot `slot` of
+// segment (b, h), which has nch chunks when the combine is fused: the only
+// chunk of a segment writes the output rows directly, and a chunk that
+// another workgroup may merge is published device-coherent.  The slot's
+// rows start at a uniform address; the lane adds a 32-bit offset.
+template <int D, bool FU>
 __device__ __forceinline__ void write_columns(const DecodeParams &p, const State<D, 1> &st,
-                                              int col0, int64_t slot, const Lane &ln) {
+                                              int col0, int64_t slot, int b, int h, int nch,
+                                              const Lane &ln) {
     const int RG = p.R * p.G;
     const int col = col0 + ln.r;
     const float l = column_sum(st.l[0]);
     if (col >= RG) return;
     const bool live = l > 0.f;
     const float inv = live ? 1.0f / l : 0.f;
-    char *obase = reinterpret_cast<char *>(p.part_o + slot * RG * D);
+    const float lse = live ? (st.m[0] + log2f(l)) * kLn2 : kNegInf;
     // accumulator blk holds d = 16 blk + 4 grp .. 16 blk + 4 grp + 3
+    if (FU && nch == 1) {
+        const int64_t row = out_row(p, b, h, col);
 #pragma unroll
-    for (int blk = 0; blk < D / 16; ++blk)
-        *reinterpret_cast<f32x4 *>(obase + (uint32_t)(col * D + 16 * blk + 4 * ln.grp) * 4u) =
-            st.o[0][blk] * inv;
-    if (ln.grp == 0)
-        p.part_lse[slot * RG + col] = live ? (st.m[0] + log2f(l)) * kLn2 : kNegInf;
+        for (int blk = 0; blk < D / 16; ++blk)
+            store_bf16x4(p.out, row * D + 16 * blk + 4 * ln.grp, st.o[0][blk] * inv);
+        if (p.out_lse && ln.grp == 0) p.out_lse[row] = lse;
+        return;
+    }
+    if constexpr (FU) {
+        const auto ro = rows_rsrc(p.part_o + slot * RG * D, (int64_t)RG * D);
+#pragma unroll
+        for (int blk = 0; blk < D / 16; ++blk)
+            publish4(ro, 4u * (uint32_t)(col * D + 16 * blk + 4 * ln.grp), st.o[0][blk] * inv);
+        if (ln.grp == 0) publish(rows_rsrc(p.part_lse + slot * RG, RG), 4u * (uint32_t)col, lse);
+    } else {
+        char *obase = reinterpret_cast<char *>(p.part_o + slot * RG * D);
+#pragma unroll
+        for (int blk = 0; blk < D / 16; ++blk)
+            *reinterpret_cast<f32x4 *>(obase + (uint32_t)(col * D + 16 * blk + 4 * ln.grp) * 4u) =
+                st.o[0][blk] * inv;
+        if (ln.grp == 0) p.part_lse[slot * RG + col] = lse;
+    }
+}
+
+// The end of descriptor `slot` in segment (b, h) on the shared-tile path:
+// every compute wave writes its columns; with the combine fused, a segment
+// of several chunks then takes a ticket and its last workgroup merges it
+// (the compute waves, nthreads threads; a staging wave takes the two
+// barriers of the ticket with them, in ticket_barriers).
+template <int D, bool FU>
+__device__ __forceinline__ void close_descriptor(const DecodeParams &p, const State<D, 1> &st,
+                                                 int &last, int64_t slot, int b, int h,
+                                                 const Lane &ln, int nthreads) {
+    int64_t k0;
+    const int nch = seg_chunks<FU>(p, b, h, k0);
+    write_columns<D, FU>(p, st, 16 * ln.w, slot, b, h, nch, ln);
+    if constexpr (FU)
+        if (nch > 1) ticket_and_merge<D>(p, b, h, k0, nch, last, nthreads);
+}
+
+// The staging wave's share of close_descriptor: the ticket's two barriers
+// when the segment has more than one chunk.
+template <bool FU>
+__device__ __forceinline__ void ticket_barriers(const DecodeParams &p, int b, int h) {
+    if constexpr (FU) {
+        int64_t k0;
+        if (seg_chunks<FU>(p, b, h, k0) > 1) {
+            __syncthreads();
+            __syncthreads();
+        }
+    }
 }
 
 // This lane's column of the shared-tile path: its query row's lag, its
@@ -1326,7 +1378,7 @@ __device__ __forceinline__ void load_q_direct(const DecodeParams &p, const Pos &
 // The drain loop of the shared-tile path (same descriptor walk as drain):
 // tile t + 1 is issued into registers before tile t is computed from LDS
 // and stored to LDS after it.
-template <class KV, int D, int NCB>
+template <class KV, int D, int NCB, bool FU>
 __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV, D> &sm,
                                              const MapSource &src, const Pos &first, int d_end,
                                              int64_t slot_base, bool by_desc) {
@@ -1373,7 +1425,8 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
         __syncthreads();   // every wave is done with the tile in LDS
 
         if (!more || n.d != cur.d) {
-            write_columns<D>(p, st, 16 * ln.w, by_desc ? (int64_t)cur.d : slot_base, ln);
+            close_descriptor<D, FU>(p, st, sm.last, by_desc ? (int64_t)cur.d : slot_base, cur.b,
+                                    cur.h, ln, 64 * NCB);
             if (!more) return;
             pre = read_ahead(src, d_end, n);
             load_q_direct<KV>(p, n, col, ln, q);
@@ -1393,7 +1446,7 @@ __device__ __forceinline__ void drain_shared(const DecodeParams &p, SharedLds<KV
 // wave's 2 NK / 64 chunks per lane and the compute waves' accumulators do
 // not add up.  Both loops take the same barriers: one when the tile in LDS
 // is no longer read, one when the next tile is in.
-template <class KV, int D, int NCB>
+template <class KV, int D, int NCB, bool FU>
 __device__ __forceinline__ void drain_shared_staged(const DecodeParams &p, SharedLds<KV, D> &sm,
                                                     const MapSource &src, const Pos &first,
                                                     int d_end, int64_t slot_base, bool by_desc) {
@@ -1416,6 +1469,7 @@ __device__ __forceinline__ void drain_shared_staged(const DecodeParams &p, Share
             const int pg_n = locate(p, far, nv_n);
             stage_load<KV, D, 64>(p, pg_n, far.h, more ? nv_n : 0, stg, ln.lane);
             __syncthreads();   // every compute wave is done with the tile in LDS
+            if (!more || n.d != cur.d) ticket_barriers<FU>(p, cur.b, cur.h);
             if (!more) return;
             if (n.d != cur.d) pre = read_ahead(src, d_end, n);
             stage_store<KV, D, 64>(sm, stg, ln.lane);
@@ -1453,7 +1507,8 @@ __device__ __forceinline__ void drain_shared_staged(const DecodeParams &p, Share
         __syncthreads();   // done with the tile in LDS
 
         if (!more || n.d != cur.d) {
-            write_columns<D>(p, st, 16 * ln.w, by_desc ? (int64_t)cur.d : slot_base, ln);
+            close_descriptor<D, FU>(p, st, sm.last, by_desc ? (int64_t)cur.d : slot_base, cur.b,
+                                    cur.h, ln, 64 * NCB);
             if (!more) return;
             pre = read_ahead(src, d_end, n);
             load_q_direct<KV>(p, n, col, ln, q);
@@ -1530,20 +1585,21 @@ constexpr int shared_waves_per_eu() {
     return (!KV::kScaled && D == 128 && NCB == 2 && SW == 0) ? 2 : 3;
 }
 
-template <class KV, int D, int NCB, int SW>
+template <class KV, int D, int NCB, int SW, bool FU>
 __global__ void __launch_bounds__(64 * (NCB + SW))
 __attribute__((amdgpu_waves_per_eu(shared_waves_per_eu<KV, D, NCB, SW>())))
 decode_shared_kernel(DecodeParams p) {
     __shared__ SharedLds<KV, D> sm;
+    if constexpr (FU) clear_empty_segments<D>(p, 64 * (NCB + SW));
     const MapLayout lay(p.B, p.Hkv, p.P);
     const int32_t *bin_off = p.map + lay.bin_off;
     const int d0 = uniform(bin_off[blockIdx.x]), d1 = uniform(bin_off[blockIdx.x + 1]);
     if (d0 >= d1) return;
     const MapSource src{p.map + lay.desc, p.map + lay.lens};
     if constexpr (SW)
-        drain_shared_staged<KV, D, NCB>(p, sm, src, src.read(d0), d1, 0, true);
+        drain_shared_staged<KV, D, NCB, FU>(p, sm, src, src.read(d0), d1, 0, true);
     else
-        drain_shared<KV, D, NCB>(p, sm, src, src.read(d0), d1, 0, true);
+        drain_shared<KV, D, NCB, FU>(p, sm, src, src.read(d0), d1, 0, true);
 }
 
 template <class KV, int D, int NCB, int SW>
@@ -1572,9 +1628,10 @@ __global__ void __launch_bounds__(64 * (NCB + SW)) static_decode_shared_kernel(D
     }
     const Pos range{0, b, h, (int)t0, (int)t1, L};
     if constexpr (SW)
-        drain_shared_staged<KV, D, NCB>(p, sm, MapSource{nullptr, nullptr}, range, 1, slot, false);
+        drain_shared_staged<KV, D, NCB, false>(p, sm, MapSource{nullptr, nullptr}, range, 1, slot,
+                                               false);
     else
-        drain_shared<KV, D, NCB>(p, sm, MapSource{nullptr, nullptr}, range, 1, slot, false);
+        drain_shared<KV, D, NCB, false>(p, sm, MapSource{nullptr, nullptr}, range, 1, slot, false);
 }
 
 // Column blocks of a workgroup: ceil(R G / 16), 1 .. 4.
@@ -1611,7 +1668,7 @@ constexpr int staging_wave(int ncb) {
 // 308.0 vs 312.4 us on two boxes), with fewer partials to combine.
 constexpr int kLdsPerCu = 160 * 1024;
 
-template <class KV, int D, int NCB, int SW>
+template <class KV, int D, int NCB, int SW, bool FU>
 unsigned shared_lds_pad() {
     constexpr bool staged_bf16 = SW != 0 && !KV::kScaled;
     if constexpr (NCB + SW != 3 && !staged_bf16) {
@@ -1621,9 +1678,8 @@ unsigned shared_lds_pad() {
             int k = 2;
             if constexpr (!staged_bf16) {
                 hipFuncAttributes a{};
-                if (hipFuncGetAttributes(&a,
-                                         (const void *)decode_shared_kernel<KV, D, NCB, SW>) !=
-                    hipSuccess)
+                if (hipFuncGetAttributes(
+                        &a, (const void *)decode_shared_kernel<KV, D, NCB, SW, FU>) != hipSuccess)
                     return 0u;
                 const int regs = (max(a.numRegs, 1) + 7) / 8 * 8;   // allocation granule
                 const int occ = min(8, 512 / regs);                  // waves per SIMD
@@ -1639,9 +1695,14 @@ unsigned shared_lds_pad() {
 template <class KV, int D, int NCB>
 hipError_t launch_shared(const DecodeParams &p, hipStream_t stream, bool dynamic, int grid) {
     constexpr int SW = staging_wave<KV, D>(NCB);
-    if (dynamic)   // (the fused combine is not offered for these workgroups)
-        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB, SW>), dim3(grid),
-                           dim3(64 * (NCB + SW)), (shared_lds_pad<KV, D, NCB, SW>()), stream, p);
+    if (dynamic && p.out)
+        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB, SW, true>), dim3(grid),
+                           dim3(64 * (NCB + SW)), (shared_lds_pad<KV, D, NCB, SW, true>()),
+                           stream, p);
+    else if (dynamic)
+        hipLaunchKernelGGL((decode_shared_kernel<KV, D, NCB, SW, false>), dim3(grid),
+                           dim3(64 * (NCB + SW)), (shared_lds_pad<KV, D, NCB, SW, false>()),
+                           stream, p);
     else
         hipLaunchKernelGGL((static_decode_shared_kernel<KV, D, NCB, SW>), dim3(grid),
                            dim3(64 * (NCB + SW)), 0, stream, p);
@@ -1717,40 +1778,62 @@ hipError_t dispatch(const DecodeParams &p, int head_dim, int kv_dtype, hipStream
 }
 
 // The dynamic kernel launch_for picks for `rows` rows with R = 1 when
-// rows <= 16 (the resident count does not depend on R otherwise).
-template <template <int> class KV, int D>
+// rows <= 16 (the resident count does not depend on R otherwise), with the
+// combine fused (FU) or not.
+template <template <int> class KV, int D, bool FU>
 const void *decode_fn(int rows, int &threads, unsigned &lds_pad) {
     constexpr int SW2 = staging_wave<KV<D>, D>(2), SW3 = staging_wave<KV<D>, D>(3),
                   SW4 = staging_wave<KV<D>, D>(4);
     const int ncb = column_blocks(rows);
     threads = ncb == 1 ? kDecodeThreads : 64 * (ncb + staging_wave<KV<D>, D>(ncb));
-    lds_pad = ncb == 3 ? shared_lds_pad<KV<D>, D, 3, SW3>() : 0u;
+    lds_pad = ncb == 3 ? shared_lds_pad<KV<D>, D, 3, SW3, FU>() : 0u;
     switch (ncb) {
     case 1:
-        lds_pad = rows <= 8 ? one_row_lds_pad<KV<D>, D, 8, 1, false, false>()
-                            : one_row_lds_pad<KV<D>, D, 16, 1, false, false>();
-        return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false, false>
-                         : (const void *)decode_kernel<KV<D>, D, 16, 1, false, false>;
-    case 2: return (const void *)decode_shared_kernel<KV<D>, D, 2, SW2>;
-    case 3: return (const void *)decode_shared_kernel<KV<D>, D, 3, SW3>;
-    default: return (const void *)decode_shared_kernel<KV<D>, D, 4, SW4>;
+        lds_pad = rows <= 8 ? one_row_lds_pad<KV<D>, D, 8, 1, false, FU>()
+                            : one_row_lds_pad<KV<D>, D, 16, 1, false, FU>();
+        return rows <= 8 ? (const void *)decode_kernel<KV<D>, D, 8, 1, false, FU>
+                         : (const void *)decode_kernel<KV<D>, D, 16, 1, false, FU>;
+    case 2: return (const void *)decode_shared_kernel<KV<D>, D, 2, SW2, FU>;
+    case 3: return (const void *)decode_shared_kernel<KV<D>, D, 3, SW3, FU>;
+    default: return (const void *)decode_shared_kernel<KV<D>, D, 4, SW4, FU>;
     }
+}
+
+template <bool FU>
+int32_t resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t rows) {
+    int n = 0;
+    int threads = 0;
+    unsigned pad = 0;
+    const void *fn = kv_dtype == HPCATTN_KV_BF16
+                         ? (head_dim == 128 ? decode_fn<Bf16, 128, FU>(rows, threads, pad)
+                                            : decode_fn<Bf16, 64, FU>(rows, threads, pad))
+                         : (head_dim == 128 ? decode_fn<Fp8, 128, FU>(rows, threads, pad)
+                                            : decode_fn<Fp8, 64, FU>(rows, threads, pad));
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, pad) != hipSuccess)
+        return 0;
+    return n;
 }
 
 }  // namespace
 
 int32_t decode_resident_per_cu(int32_t head_dim, int32_t kv_dtype, int32_t rows) {
-    int n = 0;
-    int threads = 0;
-    unsigned pad = 0;
-    const void *fn = kv_dtype == HPCATTN_KV_BF16
-                         ? (head_dim == 128 ? decode_fn<Bf16, 128>(rows, threads, pad)
-                                            : decode_fn<Bf16, 64>(rows, threads, pad))
-                         : (head_dim == 128 ? decode_fn<Fp8, 128>(rows, threads, pad)
-                                            : decode_fn<Fp8, 64>(rows, threads, pad));
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, pad) != hipSuccess)
-        return 0;
-    return n;
+    return resident_per_cu<false>(head_dim, kv_dtype, rows);
+}
+
+bool fused_keeps_residency(int32_t head_dim, int32_t kv_dtype, int32_t rows) {
+    // One answer per instance pair (dtype, head_dim, column blocks, and for
+    // one block whether rows <= 8), looked up once: 0 unknown, 1 no, 2 yes.
+    static std::atomic<int> known[2][2][5];
+    const int ncb = column_blocks(rows);
+    std::atomic<int> &k = known[kv_dtype == HPCATTN_KV_BF16 ? 0 : 1][head_dim == 128 ? 1 : 0]
+                               [ncb == 1 ? (rows <= 8 ? 0 : 1) : ncb];
+    int v = k.load(std::memory_order_relaxed);
+    if (v == 0) {
+        const int32_t n = resident_per_cu<false>(head_dim, kv_dtype, rows);
+        v = n > 0 && resident_per_cu<true>(head_dim, kv_dtype, rows) == n ? 2 : 1;
+        k.store(v, std::memory_order_relaxed);
+    }
+    return v == 2;
 }
 
 hipError_t launch_decode(const DecodeParams &p, int32_t head_dim, int32_t kv_dtype,

@@ -185,14 +185,17 @@ int check_prologue(const hpcattn_prologue_dims *d, const void *qkv, const int32_
 }
 
 bool fuse_combine(const hpcattn_dims *d, const hpcattn_task_map *map) {
-    // Fuse where it pays (measured): segments of a few chunks on the per-wave
-    // kernel.  Long segments (a mean of >= 8 chunks: the last workgroup would
-    // merge many partials alone) and workgroups of more than 16 query rows run
-    // decode and combine as two launches, with the same result.
+    // Fuse where it pays (measured): segments of a few chunks.  The last
+    // workgroup of a segment merges its chunks alone, most often at the end
+    // of the launch, so past a mean of 8 chunks (4 where a KV head serves
+    // more than 16 query rows, whose partials are larger) decode and combine
+    // run as two launches, with the same result.  Draft verification, 6 rows
+    // of 8 heads: fused 300.5 vs 310.2 us at a mean of 2 chunks (bf16),
+    // 388.1 vs 374.9 us at 5 (fp8).
     const int64_t S = (int64_t)map->batch * map->num_kv_heads;
     const int64_t mean_chunks = (S + map->num_bins - 1 + S - 1) / S;
     const int64_t rows = (int64_t)d->q_rows * (d->num_q_heads / d->num_kv_heads);
-    return mean_chunks < 8 && rows <= 16;
+    return mean_chunks < (rows <= 16 ? 8 : 4);
 }
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }

@@ -154,7 +154,10 @@ static void test_decode_paths() {
     EXPECT(check_combine(&d, &m, po, po, nullptr), HPCATTN_ERR_NULL);
     EXPECT(fuse_combine(&d, &m), true);
     hpcattn_dims rows48 = dims(4, 8, 1, 128, 6);
-    EXPECT(fuse_combine(&rows48, &m), false);
+    EXPECT(fuse_combine(&rows48, &m), true);   // a mean of 3 chunks
+    hpcattn_task_map m5 = map_for(4, 1, 16);   // a mean of 5 chunks
+    EXPECT(fuse_combine(&d, &m5), true);
+    EXPECT(fuse_combine(&rows48, &m5), false);
     hpcattn_task_map many = map_for(1, 1, I32MAX);   // mean chunks far above 8
     hpcattn_dims d1 = dims(1);
     EXPECT(fuse_combine(&d1, &many), false);

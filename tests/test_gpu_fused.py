@@ -2,11 +2,12 @@
 the fp64 oracle, through the C ABI.
 
 The fused call writes a one-chunk segment's output directly and has the last
-workgroup of a multi-chunk segment merge its partials (a per-segment ticket).
-Where fusing does not pay (a mean of 8 or more chunks per segment, or more
-than 16 query rows per KV head) the call runs decode and combine as two
-launches; the cases below cover both (small P relative to the segments fuse,
-large P and the multi-row steps of more than 16 rows do not).
+workgroup of a multi-chunk segment merge its partials (a per-segment ticket),
+in the one-row kernel and in the shared-tile multi-row kernels (with and
+without a staging wave).  Where fusing does not pay (a mean of 8 or more
+chunks per segment) the call runs decode and combine as two launches; the
+cases below cover both (small P relative to the segments fuse, large P does
+not).
 Checked here: the oracle tolerances of plain decode (bf16 max-abs <= 2e-2,
 mean-abs <= 2e-3; fp8 max-abs <= 6e-2; LSE <= 2e-2) on ragged and empty
 requests, one and many chunks per segment, several bins counts, multi-row
@@ -116,6 +117,60 @@ def test_fused_matches_two_launches_over_layers(R):
         dl = (run.out_lse - ref_l).abs().max().item()
         say("layer %d: fused vs two launches max |out| diff %.3g, |lse| diff %.3g" % (layer, d, dl))
         assert d <= 2e-2 and dl <= 1e-4
+
+
+@pytest.mark.parametrize("G,rows,kv", [(8, 6, "bf16"), (8, 6, "fp8"), (16, 4, "bf16"),
+                                       (8, 3, "bf16")])
+def test_fused_multi_row_matches_two_launches(R, G, rows, kv):
+    """Multi-row steps on the shared-tile kernels (2 to 4 column blocks, the
+    staging-wave instance at 6 rows of 8 heads): the fused call agrees with
+    decode + combine over two layers on one plan, one- and many-chunk
+    segments alike, and leaves its tickets at zero."""
+    lens = wl.seq_lens("mixed", 5)[:12]
+    prob = wl.make_problem("mixed", seed=5, device="cuda", layers=2, lens=lens, poison=True,
+                           workload=workload(2, G, 128, kv, P=40, m=1, rows=rows))
+    run = R.DecodeRunner(prob, num_bins=40, min_tiles=1)
+    run.plan()
+    for layer in range(2):
+        run.decode(layer)
+        run.combine()
+        ref_o, ref_l = run.out.clone(), run.out_lse.clone()
+        run.out.fill_(float("nan"))
+        run.decode_combine(layer)
+        sync()
+        assert int(run.tickets.abs().sum().item()) == 0
+        d = (run.out.float() - ref_o.float()).abs().max().item()
+        dl = (run.out_lse - ref_l).abs().max().item()
+        say("rows=%d G=%d %s layer %d: fused vs two launches |out| %.3g |lse| %.3g"
+            % (rows, G, kv, layer, d, dl))
+        assert d <= 2e-2 and dl <= 1e-4
+
+
+def test_fused_multi_row_graph_replays(R):
+    """The fused draft-verify step (6 rows of 8 heads, staging-wave kernel)
+    captured in a HIP graph: every replay equals eager, with eager work
+    between replays, and the tickets stay at zero."""
+    lens = wl.seq_lens("mixed", 7)[:10]
+    prob = wl.make_problem("mixed", seed=7, device="cuda", layers=2, lens=lens,
+                           workload=workload(8, 8, 128, P=64, m=1, rows=6))
+    run = R.DecodeRunner(prob, num_bins=64, min_tiles=1)
+    run.plan()
+    run.decode_combine(1)
+    sync()
+    eager = run.out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.plan()
+        run.decode_combine(0)
+        run.decode_combine(1)
+    for i in range(4):
+        run.out.zero_()
+        g.replay()
+        sync()
+        assert torch.equal(run.out, eager), "replay %d" % i
+        assert int(run.tickets.abs().sum().item()) == 0
+        run.decode_combine(0)
+        sync()
 
 
 def test_fused_graph_replays(R):

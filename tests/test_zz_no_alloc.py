@@ -97,7 +97,8 @@ def test_noalloc_unfused_paths_and_fp8(M):
     mtp = wl.make_problem("tiny", seed=2, device="cuda", poison=True,
                           lens=np.array([6, 64, 70, 1000, 3000], np.int32),
                           workload=workload(2, 8, 128, rows=6, P=16, m=1))
-    check_case(M, mtp, "6 rows of 8 heads (shared-tile kernel, two launches)", P=16, m=1)
+    check_case(M, mtp, "6 rows of 8 heads (shared-tile kernel with a staging wave, fused)", P=16,
+               m=1)
     fp8 = wl.make_problem("fp8", seed=4, device="cuda", poison=True,
                           lens=np.array([1, 64, 65, 500, 3000, 0, 129], np.int32),
                           workload=workload(2, 8, 128, "fp8", P=5, m=1))
