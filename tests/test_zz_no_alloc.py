@@ -6,8 +6,9 @@ those buffers) and against the fp64 oracle.
 Calls follow each other on one device and share the array, so the cases run
 in a row: a larger batch, then a smaller one (the second call must not see
 the first call's partials as tickets), the larger one again (the tickets
-were left at zero), the paths that do not fuse (many chunks per segment;
-more than 16 query rows), fp8, and replays of a captured graph.  The fused
+were left at zero), the path that does not fuse (many chunks per segment),
+a multi-row step on the staging-wave kernel, fp8, and replays of a captured
+graph.  The fused
 kernels and the merge order are the same in both calls, so the outputs are
 compared for equality, and with the oracle at the parity tolerances (bf16
 max-abs <= 2e-2, mean-abs <= 2e-3; fp8 max-abs <= 6e-2; LSE <= 2e-2).
