@@ -1100,7 +1100,10 @@ __device__ __forceinline__ void drain(const DecodeParams &p, MergeLds<D, GR, NCB
 //     O^T += V^T P^T over 32 tokens per v_mfma_f32_16x16x32_bf16 (the lane's
 //     tokens of two 16-token blocks form its 8 k-slots);
 //   * a wave has its columns' whole softmax state, so a descriptor's partial
-//     is written without a merge between waves.
+//     is written without a merge between waves;
+//   * with the combine fused, the compute waves also take the segment's
+//     ticket and the last workgroup's compute waves merge it; a staging
+//     wave only joins the ticket's barriers.
 // ---------------------------------------------------------------------------
 
 template <class KV, int D>
