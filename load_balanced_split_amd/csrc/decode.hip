@@ -618,7 +618,7 @@ struct MergeLds {
     // The current descriptor's Q rows of QW words (16 NCB rows, rows >= R G
     // zero), each padded by 4 dwords so that the per-tile operand reads are
     // bank-conflict free.
-    uint32_t q[16 * NCB * (QW + 4)];
+    alignas(16) uint32_t q[16 * NCB * (QW + 4)];
     int last;   // the fused combine: this workgroup merges the segment
 };
 
@@ -644,18 +644,35 @@ __device__ __forceinline__ uint8_t *k_rows_of(KRows<RB, On> &kr) {
 
 // Copy the R G query rows of (b, h) into the LDS Q rows: LDS row r G + g is
 // query row r, head h G + g (the G heads of one row are contiguous in q).
-// All threads.
+// In 16-byte chunks, all loads of a thread issued before its stores: up to
+// 16 rows (the per-wave path) that is one chunk per thread, so the staging
+// costs one memory round trip per descriptor, not one per pass.  All
+// threads.
 template <class KV, int D, int GR, int NCB, bool MR, int QW>
 __device__ __forceinline__ void stage_q(const DecodeParams &p, MergeLds<D, GR, NCB, QW> &sm, int b,
                                         int h) {
-    constexpr int RW = KV::kQRowBytes / 4, QS = RW + 4;
+    constexpr int RW = KV::kQRowBytes / 4, QS = RW + 4, CPR = RW / 4;   // CPR chunks per row
+    constexpr int NC = (16 * NCB * CPR + kDecodeThreads - 1) / kDecodeThreads;
     const int R = rows_per_req<MR>(p);
-    for (int r = 0; r < R; ++r) {
-        const char *src = reinterpret_cast<const char *>(p.q) +
-                          (((int64_t)b * R + r) * p.Hq + (int64_t)h * p.G) * KV::kQRowBytes;
-        uint32_t *dst = sm.q + r * p.G * QS;
-        for (int i = threadIdx.x; i < p.G * RW; i += kDecodeThreads)
-            dst[(i / RW) * QS + i % RW] = ldg<uint32_t>(src, 4u * (uint32_t)i);
+    const int n = R * p.G * CPR;
+    // the first row of (b, h), wave-uniform; a lane's row r G + g is r H_q + g rows on
+    const char *base = reinterpret_cast<const char *>(p.q) +
+                       ((int64_t)b * R * p.Hq + (int64_t)h * p.G) * KV::kQRowBytes;
+    u32x4 v[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int j = threadIdx.x + i * kDecodeThreads;
+        if (j < n) {
+            const int row = j / CPR, r = row / p.G, g = row - r * p.G;
+            v[i] = ldg<u32x4>(base + (int64_t)r * p.Hq * KV::kQRowBytes,
+                              (uint32_t)(g * KV::kQRowBytes + 16 * (j % CPR)));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int j = threadIdx.x + i * kDecodeThreads;
+        if (j < n)
+            *reinterpret_cast<u32x4 *>(sm.q + (j / CPR) * QS + 4 * (j % CPR)) = v[i];
     }
 }
 
