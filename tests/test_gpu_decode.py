@@ -190,6 +190,28 @@ def test_full_size_configs_sampled(R, name, npairs):
         del h, ref_o, ref_l
 
 
+def test_kv_pools_beyond_2gib(R):
+    """A request of about a million tokens among shorter ones, 8 KV heads,
+    bf16: each KV pool holds 2.4 GB, so tile addresses pass 2^31 bytes (the
+    page ids are shuffled over the whole pool).  Default bins and floor; the
+    oracle checks the long request's first and last KV head and a short
+    request, with dead slots poisoned."""
+    lens = np.array([(1 << 20) - 37, 5000, 0, 130001], np.int32)
+    w = custom_workload(8, 8, 128, "bf16", P=None, m=32)
+    prob = wl.make_problem("tiny", seed=21, device="cuda", lens=lens, poison=True, workload=w)
+    pool_bytes = prob.k_pages[0].numel() * prob.k_pages[0].element_size()
+    assert pool_bytes > (1 << 31), pool_bytes
+    run = R.DecodeRunner(prob)
+    run.plan()
+    run.decode()
+    run.combine()
+    sync()
+    pairs = [(0, 0), (0, 7), (3, 5)]
+    ref_o, ref_l = oracle_attention(host_inputs(prob), pairs)
+    compare(run.out, run.out_lse, ref_o, ref_l, rows_of(pairs, 8), False,
+            "pools of %.2f GB" % (pool_bytes / 1e9))
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_maximum_batch(R, kv):
     """The largest batch the library takes (8192 requests), ragged lengths
