@@ -190,14 +190,18 @@ def test_full_size_configs_sampled(R, name, npairs):
         del h, ref_o, ref_l
 
 
-def test_kv_pools_beyond_2gib(R):
-    """A request of about a million tokens among shorter ones, 8 KV heads,
-    bf16: each KV pool holds 2.4 GB, so tile addresses pass 2^31 bytes (the
-    page ids are shuffled over the whole pool).  Default bins and floor; the
-    oracle checks the long request's first and last KV head and a short
-    request, with dead slots poisoned."""
-    lens = np.array([(1 << 20) - 37, 5000, 0, 130001], np.int32)
-    w = custom_workload(8, 8, 128, "bf16", P=None, m=32)
+@pytest.mark.parametrize("kv,rows,long_len", [("bf16", 1, (1 << 20) - 37),
+                                               ("fp8", 1, (1 << 21) - 37),
+                                               ("bf16", 6, (1 << 20) - 37)])
+def test_kv_pools_beyond_2gib(R, kv, rows, long_len):
+    """A request of one or two million tokens among shorter ones, 8 KV heads:
+    each KV pool holds more than 2^31 bytes, so tile addresses pass 2^31
+    (the page ids are shuffled over the whole pool).  One-row bf16 and fp8,
+    and the draft-verify staging-wave kernel.  Default bins and floor; the
+    oracle checks the long request's last KV head and a short request (and
+    the long one's first head for one row), with dead slots poisoned."""
+    lens = np.array([long_len, 5000, 0, 130001], np.int32)
+    w = wl.Workload("custom", None, 8, 64, 128, kv, min_tiles=32, q_rows=rows)
     prob = wl.make_problem("tiny", seed=21, device="cuda", lens=lens, poison=True, workload=w)
     pool_bytes = prob.k_pages[0].numel() * prob.k_pages[0].element_size()
     assert pool_bytes > (1 << 31), pool_bytes
@@ -206,10 +210,19 @@ def test_kv_pools_beyond_2gib(R):
     run.decode()
     run.combine()
     sync()
-    pairs = [(0, 0), (0, 7), (3, 5)]
+    pairs = [(0, 7), (3, 5)] + ([(0, 0)] if rows == 1 else [])
     ref_o, ref_l = oracle_attention(host_inputs(prob), pairs)
-    compare(run.out, run.out_lse, ref_o, ref_l, rows_of(pairs, 8), False,
-            "pools of %.2f GB" % (pool_bytes / 1e9))
+    what = "%s, %d row(s), pools of %.2f GB" % (kv, rows, pool_bytes / 1e9)
+    if rows == 1:
+        compare(run.out, run.out_lse, ref_o, ref_l, rows_of(pairs, 8), kv == "fp8", what)
+    else:
+        B = len(lens)
+        o = run.out.view(B * rows, 64, 128)
+        l = run.out_lse.view(B * rows, 64)
+        cmp_rows = [(b * rows + r, h * 8 + g) for b, h in pairs for r in range(rows)
+                    for g in range(8)]
+        compare(o, l, ref_o.reshape(B * rows, 64, 128), ref_l.reshape(B * rows, 64), cmp_rows,
+                False, what)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
