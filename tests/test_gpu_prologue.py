@@ -228,3 +228,58 @@ def test_prologue_with_no_tokens_writes_nothing(H, fp8):
         assert (sc["k_scale"] == -1.0).all() and (sc["v_scale"] == -1.0).all()
     else:
         assert (kp.float() == 0.3125).all() and (vp.float() == 0.3125).all()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prologue_into_pools_beyond_2gib(H, fp8):
+    """KV stored into a pool of 2.6 GB (bf16, 20000 pages; fp8, 40000): the
+    tokens' cache slots lie in the pool's upper half, so the byte offsets of
+    the stores pass 2^31.  The stored K/V (values, or codes
+    and scales) match the oracle, and every page no token was sent to keeps
+    its sentinel."""
+    T, Hq, Hkv, D = 512, 64, 8, 128
+    flags = H.PROLOGUE_ROPE | H.PROLOGUE_HADAMARD
+    num_pages = 40000 if fp8 else 20000
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    rng = np.random.default_rng(77)
+    qkv = (torch.randn((T, (Hq + 2 * Hkv) * D), generator=gen, device="cuda") * 3.0) \
+        .to(torch.bfloat16)
+    pos = torch.from_numpy(rng.integers(0, 131072, size=T).astype(np.int32)).cuda()
+    sl = rng.choice(np.arange(num_pages // 2 * 64, num_pages * 64), size=T,
+                    replace=False).astype(np.int32)
+    sl[1::7] = -1
+    slots = torch.from_numpy(sl).cuda()
+    qw = torch.from_numpy(rng.uniform(0.5, 1.5, D).astype(np.float32)).cuda()
+    kw = torch.from_numpy(rng.uniform(0.5, 1.5, D).astype(np.float32)).cuda()
+    q_out, kp, vp, sc = run_gpu(H, qkv, pos, slots, qw, kw, Hq, Hkv, D, num_pages, fp8, flags)
+    pool_bytes = kp.numel() * kp.element_size()
+    assert pool_bytes > (1 << 31), pool_bytes
+    ref = oracle.prologue(wl.as_numpy(qkv), pos.cpu().numpy(), num_q_heads=Hq,
+                          num_kv_heads=Hkv, head_dim=D, q_norm_w=qw.cpu().numpy(),
+                          k_norm_w=kw.cpu().numpy(), eps=1e-6, rope=True, rope_base=10000.0,
+                          hadamard=True)
+    stored = np.nonzero(sl >= 0)[0]
+    page = torch.from_numpy((sl[stored] // 64).astype(np.int64)).cuda()
+    slot = torch.from_numpy((sl[stored] % 64).astype(np.int64)).cuda()
+    what = "pool of %.2f GB, %s" % (pool_bytes / 1e9, "fp8" if fp8 else "bf16")
+    touched = torch.zeros(num_pages, dtype=torch.bool, device="cuda")
+    touched[page] = True
+    sentinel = 0x5A if fp8 else 0.3125
+    assert bool((kp[~touched] == sentinel).all()) and bool((vp[~touched] == sentinel).all()), what
+    if not fp8:
+        kg = kp[page, :, slot].float().cpu().numpy()
+        vg = vp[page, :, slot].float().cpu().numpy()
+        kr, vr = ref["k_val"][stored], ref["v_val"][stored]
+        assert (np.abs(kg - kr) <= 2.0 ** -8 * np.abs(kr) + 1e-5).all(), what
+        np.testing.assert_array_equal(vg, vr)
+    else:
+        ks = sc["k_scale"][page, :, slot].cpu().numpy()
+        vs = sc["v_scale"][page, :, slot].cpu().numpy()
+        np.testing.assert_allclose(ks, ref["k_scale"][stored], rtol=1e-5)
+        np.testing.assert_allclose(vs, ref["v_scale"][stored], rtol=1e-5)
+        check_codes(kp[page, :, slot].cpu().numpy(), ref["k_code"][stored],
+                    ref["k_val"][stored], ref["k_scale"][stored], what + " k")
+        check_codes(vp[page, :, slot].cpu().numpy(), ref["v_code"][stored],
+                    ref["v_val"][stored], ref["v_scale"][stored], what + " v")
+    say(what, "ok")
