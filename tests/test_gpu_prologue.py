@@ -283,3 +283,47 @@ def test_prologue_into_pools_beyond_2gib(H, fp8):
         check_codes(vp[page, :, slot].cpu().numpy(), ref["v_code"][stored],
                     ref["v_val"][stored], ref["v_scale"][stored], what + " v")
     say(what, "ok")
+
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prologue_graph_replays(H, fp8):
+    """The prologue captured in a HIP graph: from the same starting buffers,
+    every replay writes exactly what the eager call wrote (Q out, the cache
+    pages, fp8 scales), with eager calls on the same buffers between
+    replays."""
+    T, Hq, Hkv, D = 300, 64, 8, 128
+    flags = H.PROLOGUE_ROPE | H.PROLOGUE_HADAMARD
+    num_pages = (T + 63) // 64 + 3
+    qkv, pos, slots, qw, kw = make_inputs(T, Hq, Hkv, D, num_pages, seed=5)
+    q0, k0, v0, s0 = run_gpu(H, qkv, pos, slots, qw, kw, Hq, Hkv, D, num_pages, fp8, flags)
+    dims = H.hpcattn_prologue_dims(T, Hq, Hkv, D, num_pages,
+                                   H.KV_FP8_E4M3 if fp8 else H.KV_BF16, flags, 1e-6, 10000.0)
+    sentinel = 0x5A if fp8 else 0.3125
+    q_out, kp, vp = torch.empty_like(q0), torch.empty_like(k0), torch.empty_like(v0)
+    sc = {n: torch.empty_like(t) for n, t in s0.items()}
+
+    def reset():   # the starting contents run_gpu gave the eager call
+        q_out.zero_()
+        kp.fill_(sentinel)
+        vp.fill_(sentinel)
+        for n, t in sc.items():
+            t.fill_(0.0 if n == "q_scale" else -1.0)
+
+    def call():
+        H.hpcattn_prologue(dims, qkv, pos, slots, q_out, kp, vp, q_norm_w=qw, k_norm_w=kw, **sc)
+
+    reset()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        reset()
+        g.replay()
+        sync()
+        assert torch.equal(q_out, q0) and torch.equal(kp, k0) and torch.equal(vp, v0), i
+        for n, t in sc.items():
+            assert torch.equal(t, s0[n]), (n, i)
+        reset()
+        call()   # eager work on the same buffers between replays
+        sync()
