@@ -57,3 +57,37 @@ def test_graph_replay_matches_eager(R, name, lens):
         other.run()            # eager work between replays
         sync()
     say(name, "graph replays match eager bit for bit")
+
+
+def test_two_streams_at_once_match_one_after_the_other(R):
+    """Two independent decode steps enqueued on two streams, their kernels
+    free to overlap (bf16 one-row, and the fp8 fused call on the staging-wave
+    kernel): each result equals the same step run alone.  The library keeps
+    no state between calls that the two could share."""
+    a = R.DecodeRunner(wl.make_problem("mixed", seed=21, device="cuda", layers=1,
+                                       lens=wl.seq_lens("mixed", 21)[:24]))
+    # 8 requests of 6 rows over 64 bins: a mean of 2 chunks per segment, so
+    # the call fuses
+    b = R.DecodeRunner(wl.make_problem("mtp_fp8", seed=22, device="cuda", layers=1,
+                                       lens=wl.seq_lens("mtp_fp8", 22)[:8]), num_bins=64)
+    a.run(0)
+    b.plan()
+    b.decode_combine(0)
+    sync()
+    ref_a, ref_b = a.out.clone(), b.out.clone()
+    a.out.zero_()
+    b.out.zero_()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    sync()
+    for rep in range(3):
+        a.plan(sa)
+        b.plan(sb)
+        a.decode(0, sa)
+        b.decode_combine(0, sb)
+        a.combine(sa)
+        sync()
+        assert torch.equal(a.out, ref_a) and torch.equal(b.out, ref_b), rep
+        assert int(b.tickets.abs().sum().item()) == 0
+        a.out.zero_()
+        b.out.zero_()
+        sync()
